@@ -1,0 +1,194 @@
+"""Checks that pin the oracle to facts fixed by the page
+"Window-Aligned Sequence Parallelism (SeedVR2)", section "Window layouts"
+(size formulas, regular and shifted methods, exact partition, clipping instead
+of wrapping, enumeration order, canonical id) and by mathematics (masked
+softmax attention, closed forms).  Each check raises AssertionError on
+failure; the oracle tests call them on real inputs and the mutation tests call
+them on a deliberately broken oracle to show they catch the mistake.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- planner pins
+
+def check_worked_examples(oracle_plan):
+    """Hand-derived worked examples (tests/golden/plan_worked_examples.json)."""
+    g = load_golden("plan_worked_examples.json")
+    for ex in g["examples"]:
+        T, H, W = ex["grid"]
+        nt, nh, nw = ex["num_windows_param"]
+        assert list(oracle_plan.window_size(T, H, W, nt, nh, nw)) == ex["window_size"], ex["name"]
+        for mname, method in (("regular", oracle_plan.REGULAR), ("shifted", oracle_plan.SHIFTED)):
+            want = ex[mname]
+            p = oracle_plan.plan(T, H, W, nt, nh, nw, method)
+            if "perm" in want:
+                assert p.perm == want["perm"], (ex["name"], mname)
+            if want.get("perm_is_identity"):
+                assert p.perm == list(range(T * H * W)), (ex["name"], mname)
+            if "cu_seqlens" in want:
+                assert p.cu_seqlens == want["cu_seqlens"], (ex["name"], mname)
+            if "boxes" in want:
+                assert [list(b) for b in p.boxes] == want["boxes"], (ex["name"], mname)
+            if "num_windows" in want:
+                assert p.num_windows == want["num_windows"], (ex["name"], mname)
+            if "first_window_tokens" in want:
+                assert p.cu_seqlens[1] == want["first_window_tokens"], (ex["name"], mname)
+            if "last_window_tokens" in want:
+                assert p.cu_seqlens[-1] - p.cu_seqlens[-2] == want["last_window_tokens"], (ex["name"], mname)
+            if "max_seqlen" in want:
+                assert p.max_seqlen == want["max_seqlen"], (ex["name"], mname)
+            if "axis_segments" in want:
+                segs = want["axis_segments"]
+                assert [list(s) for s in oracle_plan.axis_segments(T, p.wt, method)] == segs["t"]
+                assert [list(s) for s in oracle_plan.axis_segments(H, p.wh, method)] == segs["h"]
+                assert [list(s) for s in oracle_plan.axis_segments(W, p.ww, method)] == segs["w"]
+
+
+def check_size_invariance(oracle_plan):
+    """Section "Motivation": the window size is normalised to the 720p area, so
+    a higher resolution grows the number of windows, never their size."""
+    grids = [(21, 45, 80), (21, 68, 120), (21, 90, 160)]
+    sizes = [oracle_plan.window_size(T, H, W, 4, 3, 3) for T, H, W in grids]
+    assert sizes[0] == sizes[1] == sizes[2] == (6, 15, 27), sizes
+    for method in (oracle_plan.REGULAR, oracle_plan.SHIFTED):
+        counts = [oracle_plan.plan(T, H, W, 4, 3, 3, method).num_windows for T, H, W in grids]
+        assert counts[0] < counts[1] < counts[2], counts
+
+
+def check_temporal_cap(oracle_plan):
+    """Size formula block: the temporal window is ceil(min(T, 30) / nt)."""
+    for nt in (1, 2, 3, 4, 7):
+        assert oracle_plan.window_size(30, 45, 80, nt, 3, 3)[0] == math.ceil(30 / nt)
+        assert oracle_plan.window_size(31, 45, 80, nt, 3, 3)[0] == math.ceil(30 / nt)
+        assert oracle_plan.window_size(200, 45, 80, nt, 3, 3)[0] == math.ceil(30 / nt)
+        assert oracle_plan.window_size(5, 45, 80, nt, 3, 3)[0] == math.ceil(5 / nt)
+
+
+def check_exact_scales(oracle_plan):
+    """Grids whose area is the reference area over a perfect square have an
+    exact scale, so the rescaled extents are known integers; the two tie grids
+    check Python's round-half-to-even (22.5 -> 22, 7.5 -> 8)."""
+    assert oracle_plan.window_size(1, 45, 80, 1, 1, 1) == (1, 45, 80)        # scale 1
+    assert oracle_plan.window_size(1, 9, 16, 1, 1, 1) == (1, 45, 80)         # scale 5
+    assert oracle_plan.window_size(1, 90, 160, 1, 1, 1) == (1, 45, 80)       # scale 1/2
+    assert oracle_plan.window_size(1, 9, 64, 1, 1, 1) == (1, 22, 160)        # scale 5/2, 22.5 -> 22
+    assert oracle_plan.window_size(1, 3, 192, 1, 1, 1) == (1, 8, 480)        # scale 5/2, 7.5 -> 8
+    assert oracle_plan.window_size(1, 45, 80, 1, 3, 3) == (1, 15, 27)
+    assert oracle_plan.window_size(7, 45, 80, 2, 4, 7) == (4, 12, 12)
+
+
+def _label_regular(x, w):
+    return x // w
+
+
+def _label_shifted(x, n, w):
+    """Segment index of coordinate x under the half-window shift, written as a
+    per-coordinate closed form: with offset o = floor(w/2) the cuts are
+    o, o+w, o+2w, ...; a zero-width first segment (o == 0) is not counted."""
+    if w >= n:
+        return 0
+    o = w // 2
+    idx = (x - o) // w + 1 if x >= o else 0
+    return idx - 1 if o == 0 else idx
+
+
+def check_plan_invariants(oracle_plan, p, T, H, W, nt, nh, nw, method):
+    """Exact partition, box membership, enumeration order, row-major tokens,
+    canonical ids (windowing np.arange), per-coordinate labelling twin."""
+    L = T * H * W
+    perm = np.asarray(p.perm, dtype=np.int64)
+    assert perm.shape == (L,)
+    assert np.array_equal(np.sort(perm), np.arange(L)), "not a partition"
+    inv = np.asarray(p.inv, dtype=np.int64)
+    assert np.array_equal(inv[perm], np.arange(L))
+    cu = np.asarray(p.cu_seqlens, dtype=np.int64)
+    assert cu[0] == 0 and cu[-1] == L and len(cu) == p.num_windows + 1
+    vols = [(b[1] - b[0]) * (b[3] - b[2]) * (b[5] - b[4]) for b in p.boxes]
+    assert all(v > 0 for v in vols)
+    assert np.array_equal(np.diff(cu), vols)
+    # windowing np.arange: the window-order ids are the row-major flattening of
+    # each box of the canonical id grid, boxes in enumeration order
+    grid = np.arange(L).reshape(T, H, W)
+    twin = np.concatenate([grid[t0:t1, h0:h1, w0:w1].ravel() for (t0, t1, h0, h1, w0, w1) in p.boxes])
+    assert np.array_equal(twin, perm), "perm differs from windowing arange"
+    # enumeration order: w outermost, h, t innermost
+    keys = [(b[4], b[2], b[0]) for b in p.boxes]
+    assert keys == sorted(keys) and len(set(keys)) == len(keys), "enumeration order"
+    # per-coordinate labelling twin: window of each token from closed-form labels
+    wt, wh, ww = p.wt, p.wh, p.ww
+    if method == oracle_plan.REGULAR:
+        lt = [_label_regular(x, wt) for x in range(T)]
+        lh = [_label_regular(x, wh) for x in range(H)]
+        lw = [_label_regular(x, ww) for x in range(W)]
+    else:
+        lt = [_label_shifted(x, T, wt) for x in range(T)]
+        lh = [_label_shifted(x, H, wh) for x in range(H)]
+        lw = [_label_shifted(x, W, ww) for x in range(W)]
+    nT, nH = max(lt) + 1, max(lh) + 1
+    assert p.num_windows == nT * nH * (max(lw) + 1)
+    win_of_pos = np.repeat(np.arange(p.num_windows), np.diff(cu))
+    for c in range(L):
+        t, rem = divmod(c, H * W)
+        h, w = divmod(rem, W)
+        want = (lw[w] * nH + lh[h]) * nT + lt[t]
+        assert win_of_pos[inv[c]] == want, ("label twin", c)
+    # clipped, not rolled: no window on a split axis holds both ends of it
+    for (t0, t1, h0, h1, w0, w1) in p.boxes:
+        for lo, hi, n, nseg in ((t0, t1, T, nT), (h0, h1, H, nH), (w0, w1, W, max(lw) + 1)):
+            assert 0 <= lo < hi <= n
+            if nseg > 1:
+                assert not (lo == 0 and hi == n)
+
+
+def check_shift_geometry(oracle_plan, n, w):
+    """Regular segments are full windows except a short last one; shifted
+    segments start with a half window (floor(w/2)), continue with full windows
+    and end clipped at n; a covering window is not shifted."""
+    reg = oracle_plan.regular_segments(n, w)
+    assert reg[0][0] == 0 and reg[-1][1] == n
+    assert all(b - a == w for a, b in reg[:-1]) and 0 < reg[-1][1] - reg[-1][0] <= w
+    sh = oracle_plan.shifted_segments(n, w)
+    assert sh[0][0] == 0 and sh[-1][1] == n
+    assert all(sh[i][1] == sh[i + 1][0] for i in range(len(sh) - 1))
+    if w >= n:
+        assert sh == [(0, n)]
+    elif w == 1:
+        assert sh == reg
+    else:
+        assert sh[0] == (0, w // 2)
+        assert all(b - a == w for a, b in sh[1:-1])
+        assert 0 < sh[-1][1] - sh[-1][0] <= w
+        assert sh != reg
+
+
+# --------------------------------------------------------------- attention pins
+
+def torch_sdpa_masked(qc, kc, vc, window_of_token, scale):
+    """Library routine: torch's scaled_dot_product_attention in float64 on the
+    CPU, over all tokens in canonical order with a boolean same-window mask."""
+    import torch
+    F = torch.nn.functional
+    B, L, Hh, D = qc.shape
+    win = torch.as_tensor(np.asarray(window_of_token))
+    mask = win[:, None] == win[None, :]
+    q = torch.as_tensor(qc).permute(0, 2, 1, 3).contiguous()
+    k = torch.as_tensor(kc).permute(0, 2, 1, 3).contiguous()
+    v = torch.as_tensor(vc).permute(0, 2, 1, 3).contiguous()
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    s = (q @ k.transpose(-1, -2)) * scale
+    s = s.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o.permute(0, 2, 1, 3).numpy(), lse.numpy()

@@ -1,0 +1,224 @@
+"""Plant plausible mistakes in the oracle (CPU only, restored after each test)
+and check that at least one pin catches each of them."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as oatt
+from oracle import permute as operm
+from oracle import plan as oplan
+from tests import oracle_pins as pins
+
+
+def _plan_pins_fail():
+    try:
+        pins.check_worked_examples(oplan)
+        pins.check_size_invariance(oplan)
+        pins.check_temporal_cap(oplan)
+        pins.check_exact_scales(oplan)
+        for n in range(1, 20):
+            for w in range(1, 22):
+                pins.check_shift_geometry(oplan, n, w)
+        for grid in [(1, 3, 4), (3, 5, 7), (4, 6, 6)]:
+            for ns in [(1, 26, 35), (2, 17, 9), (3, 9, 9), (1, 5, 33)]:
+                for m in (oplan.REGULAR, oplan.SHIFTED):
+                    p = oplan.plan(*grid, *ns, m)
+                    pins.check_plan_invariants(oplan, p, *grid, *ns, m)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def test_unmutated_oracle_passes():
+    assert not _plan_pins_fail()
+
+
+def _plan_t_outer(T, H, W, nt, nh, nw, method):
+    """Enumeration with t outermost instead of w outermost."""
+    wt, wh, ww = oplan.window_size(T, H, W, nt, nh, nw)
+    p = oplan.Plan(T, H, W, method, wt, wh, ww)
+    p.cu_seqlens.append(0)
+    for (t0, t1) in oplan.axis_segments(T, wt, method):
+        for (h0, h1) in oplan.axis_segments(H, wh, method):
+            for (w0, w1) in oplan.axis_segments(W, ww, method):
+                p.boxes.append((t0, t1, h0, h1, w0, w1))
+                for t in range(t0, t1):
+                    for h in range(h0, h1):
+                        for w in range(w0, w1):
+                            p.perm.append((t * H + h) * W + w)
+                p.cu_seqlens.append(len(p.perm))
+    p.inv = [0] * len(p.perm)
+    for j, c in enumerate(p.perm):
+        p.inv[c] = j
+    return p
+
+
+def _plan_transposed_id(T, H, W, nt, nh, nw, method):
+    """Canonical id with h and w swapped."""
+    p = _ORIG_PLAN(T, H, W, nt, nh, nw, method)
+    p.perm = []
+    for (t0, t1, h0, h1, w0, w1) in p.boxes:
+        for t in range(t0, t1):
+            for h in range(h0, h1):
+                for w in range(w0, w1):
+                    p.perm.append((t * W + w) * H + h)
+    p.inv = [0] * len(p.perm)
+    for j, c in enumerate(p.perm):
+        if c < len(p.inv):
+            p.inv[c] = j
+    return p
+
+
+_ORIG_PLAN = oplan.plan
+
+
+def _size_floor(T, H, W, nt, nh, nw):
+    scale = math.sqrt(oplan.REFERENCE_AREA / (H * W))
+    rh, rw = round(H * scale), round(W * scale)
+    return min(T, 30) // nt or 1, rh // nh or 1, rw // nw or 1
+
+
+def _size_trunc_round(T, H, W, nt, nh, nw):
+    scale = math.sqrt(oplan.REFERENCE_AREA / (H * W))
+    rh, rw = int(H * scale), int(W * scale)
+    return -(-min(T, 30) // nt), -(-rh // nh), -(-rw // nw)
+
+
+def _size_no_cap(T, H, W, nt, nh, nw):
+    scale = math.sqrt(oplan.REFERENCE_AREA / (H * W))
+    rh, rw = round(H * scale), round(W * scale)
+    return -(-T // nt), -(-rh // nh), -(-rw // nw)
+
+
+def _shifted_ceil_half(n, w):
+    """The rejected reading: cut k*w - floor(w/2)."""
+    if w >= n:
+        return [(0, n)]
+    cuts = [0] + [k * w - w // 2 for k in range(1, n + 2) if 0 < k * w - w // 2 < n] + [n]
+    return [(a, b) for a, b in zip(cuts, cuts[1:]) if b > a]
+
+
+def _shifted_rolled(n, w):
+    """Cyclic shift: the last partial window wraps around to the first."""
+    if w >= n:
+        return [(0, n)]
+    o = w // 2
+    return [(a + o, min(a + o + w, n)) for a in range(0, n - o, w)] + ([(0, o)] if o else [])
+
+
+def _shifted_always(n, w):
+    """Shift even when the window covers the axis."""
+    o = w // 2
+    cuts = [0] + [o + k * w for k in range(n + 1) if 0 < o + k * w < n] + [n]
+    return [(a, b) for a, b in zip(cuts, cuts[1:]) if b > a]
+
+
+def _regular_unclipped(n, w):
+    return [(k * w, (k + 1) * w) for k in range(-(-n // w))]
+
+
+PLAN_MUTANTS = {
+    "t_outer_enumeration": ("plan", _plan_t_outer),
+    "transposed_canonical_id": ("plan", _plan_transposed_id),
+    "floor_instead_of_ceil": ("window_size", _size_floor),
+    "truncating_round": ("window_size", _size_trunc_round),
+    "no_temporal_cap": ("window_size", _size_no_cap),
+    "shift_cut_rejected_reading": ("shifted_segments", _shifted_ceil_half),
+    "rolled_shift": ("shifted_segments", _shifted_rolled),
+    "shift_covering_axis": ("shifted_segments", _shifted_always),
+    "regular_unclipped": ("regular_segments", _regular_unclipped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PLAN_MUTANTS))
+def test_plan_mutant_is_caught(name, monkeypatch):
+    attr, fn = PLAN_MUTANTS[name]
+    monkeypatch.setattr(oplan, attr, fn)
+    assert _plan_pins_fail(), f"pins did not catch mutant {name}"
+
+
+# ------------------------------------------------------------------ attention
+
+def _head_scale_inverted(q, k, v, scale):
+    return _ORIG_HEAD(q, k, v, 1.0 / scale)
+
+
+def _head_softmax_wrong_axis(q, k, v, scale):
+    s = (q @ k.T) * scale
+    e = np.exp(s - s.max(axis=0, keepdims=True))
+    z = e.sum(axis=0, keepdims=True)
+    return (e / z) @ v, np.log(z[0]) + s.max(axis=0)
+
+
+def _head_transposed_p(q, k, v, scale):
+    s = (q @ k.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    return (e / z).T @ v, (m + np.log(z))[:, 0]
+
+
+def _head_k_for_v(q, k, v, scale):
+    return _ORIG_HEAD(q, k, k, scale)
+
+
+_ORIG_HEAD = oatt.head_attention
+
+
+def _window_attention_off_by_one(q, k, v, cu, scale=None):
+    cu = list(cu)
+    cu2 = [cu[0]] + [min(c + 1, cu[-1]) for c in cu[1:-1]] + [cu[-1]]
+    return _ORIG_WA(q, k, v, cu2, scale)
+
+
+_ORIG_WA = oatt.window_attention
+
+
+def _attention_pins_fail():
+    try:
+        T, H, W, nt, nh, nw = 3, 5, 7, 2, 17, 9
+        p = oplan.plan(T, H, W, nt, nh, nw, oplan.SHIFTED)
+        L, Hh, D = T * H * W, 2, 16
+        rng = np.random.default_rng(3)
+        qc, kc, vc = (rng.standard_normal((1, L, Hh, D)) for _ in range(3))
+        ow, lw = oatt.window_attention(operm.gather(qc, p.perm), operm.gather(kc, p.perm),
+                                       operm.gather(vc, p.perm), p.cu_seqlens)
+        o = operm.scatter(ow, p.perm)
+        win = np.empty(L, dtype=np.int64)
+        for i in range(p.num_windows):
+            win[np.asarray(p.perm[p.cu_seqlens[i]:p.cu_seqlens[i + 1]])] = i
+        ot, lt = pins.torch_sdpa_masked(qc, kc, vc, win, 1.0 / math.sqrt(D))
+        assert np.max(np.abs(o - ot)) < 1e-12
+        assert np.max(np.abs(lw[:, :, p.inv] - lt)) < 1e-12
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+ATTN_MUTANTS = {
+    "scale_inverted": ("head_attention", _head_scale_inverted),
+    "softmax_wrong_axis": ("head_attention", _head_softmax_wrong_axis),
+    "transposed_probabilities": ("head_attention", _head_transposed_p),
+    "keys_used_as_values": ("head_attention", _head_k_for_v),
+    "window_bounds_off_by_one": ("window_attention", _window_attention_off_by_one),
+}
+
+
+def test_unmutated_attention_passes():
+    assert not _attention_pins_fail()
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_MUTANTS))
+def test_attention_mutant_is_caught(name, monkeypatch):
+    attr, fn = ATTN_MUTANTS[name]
+    monkeypatch.setattr(oatt, attr, fn)
+    assert _attention_pins_fail(), f"pins did not catch mutant {name}"
+
+
+def test_permute_mutant_is_caught(monkeypatch):
+    # scatter written as a gather (perm and its inverse confused)
+    monkeypatch.setattr(operm, "scatter", lambda x, perm: x[:, np.argsort(np.argsort(perm))])
+    p = oplan.plan(1, 3, 4, 1, 26, 35, oplan.REGULAR)
+    x = np.arange(12)[None, :]
+    assert not np.array_equal(operm.scatter(operm.gather(x, p.perm), p.perm), x)
