@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the window-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+entry gather of Q, K, V into the first layout, then for every attention layer
+of the workload's schedule a fused layout transition of Q, K, V (when the
+layout changes) and window attention, then the exit scatter of the last
+layer's output back to canonical order.  Inputs are resident in HBM before
+the timed region starts; nothing is allocated inside it.
+
+Prints ONE JSON line.  `value` is whole-step useful attention TFLOP/s
+(useful flops / step time); the attention kernels alone and the permute
+kernels alone are reported beside it, each against its roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video_21x45x80")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Step:
+    """Pre-allocated buffers and the launch sequence of one step."""
+
+    def __init__(self, w, wa, torch, dev):
+        from window_attention_amd.inputs import qkv
+        self.w, self.wa, self.torch = w, wa, torch
+        method = {"R": wa.REGULAR, "S": wa.SHIFTED}
+        self.plans = {m: wa.plan_cached(w.T, w.H, w.W, w.nt, w.nh, w.nw, method[m], device=dev) for m in "RS"}
+        self.q, self.k, self.v = qkv(w.wid, w.batch, w.L, w.heads, w.head_dim, w.sigma, device=dev)
+        e = torch.empty_like
+        self.bufs = [[e(self.q), e(self.q), e(self.q)], [e(self.q), e(self.q), e(self.q)]]
+        self.o = e(self.q)
+        self.out = e(self.q)
+        self.stream = torch.cuda.current_stream()
+        self.attn_events = []
+        self.perm_events = []
+        self.row_bytes = w.heads * w.head_dim * 2
+        # algorithmic work
+        from window_attention_amd.workloads import Workload  # noqa: F401
+        self.attn_flops = []
+        cur = w.entry
+        self.n_perm = 3  # entry gather
+        for lay in w.schedule:
+            if lay != cur:
+                self.n_perm += 3
+                cur = lay
+            cu = self.plans[lay].cu_seqlens.cpu().tolist()
+            self.attn_flops.append(sum(4 * (cu[i + 1] - cu[i]) ** 2 * w.head_dim for i in range(len(cu) - 1))
+                                   * w.heads * w.batch)
+        self.n_perm += 1  # exit scatter
+        # one read and one write of every row, plus the index reads (4 B per
+        # row for gather/scatter, 8 B for a transition)
+        self.perm_bytes_data = 2 * w.batch * w.L * self.row_bytes
+
+    def run(self, timed=False):
+        wa, w, torch = self.wa, self.w, self.torch
+        ev = (lambda: torch.cuda.Event(enable_timing=True)) if timed else None
+        cur = w.entry
+        src = self.bufs[0]
+
+        def perm_launch(fn):
+            if timed:
+                a, b = ev(), ev()
+                a.record(self.stream)
+                fn()
+                b.record(self.stream)
+                self.perm_events.append((a, b))
+            else:
+                fn()
+
+        p = self.plans[cur]
+        for x, dst in zip((self.q, self.k, self.v), src):
+            perm_launch(lambda x=x, dst=dst: wa.gather(x, p.perm, out=dst))
+        side = 0
+        for lay in w.schedule:
+            if lay != cur:
+                pa, pb = self.plans[cur], self.plans[lay]
+                dst = self.bufs[1 - side]
+                for s_, d_ in zip(src, dst):
+                    perm_launch(lambda s_=s_, d_=d_: wa.transition(s_, pa.inv, pb.perm, out=d_))
+                side = 1 - side
+                src = dst
+                cur = lay
+            pl = self.plans[lay]
+            if timed:
+                a, b = ev(), ev()
+                a.record(self.stream)
+            wa.attn_fwd(src[0], src[1], src[2], pl.cu_seqlens, pl.max_seqlen, out=self.o)
+            if timed:
+                b.record(self.stream)
+                self.attn_events.append((a, b))
+        pl = self.plans[cur]
+        perm_launch(lambda: wa.scatter(self.o, pl.perm, out=self.out))
+
+
+def cpu_baseline(w, seconds):
+    """The oracle as it stands, timed on the host cores on a bounded sample
+    of the same workload: per-window fp64 attention over the first windows of
+    the first layer's layout, head by head, until the time budget is used."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import permute as operm
+    from oracle import plan as oplan
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    method = 0 if w.schedule[0] == "R" else 1
+    p = oplan.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, method)
+    t_plan = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    D = w.head_dim
+    flops = 0
+    done = 0
+    t0 = time.perf_counter()
+    scale = 1.0 / math.sqrt(D)
+    for i in range(p.num_windows):
+        n = p.cu_seqlens[i + 1] - p.cu_seqlens[i]
+        q, k, v = (rng.standard_normal((n, D)) for _ in range(3))
+        for h in range(w.heads):
+            oatt.head_attention(q, k, v, scale)
+            flops += 4 * n * n * D
+            done += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        if time.perf_counter() - t0 > seconds:
+            break
+    t_attn = time.perf_counter() - t0
+    # permute sample: gather of 4096 canonical rows of the workload's row size
+    rows = min(4096, w.L)
+    x = rng.integers(0, 2 ** 16, size=(1, w.L, w.heads * D), dtype=np.uint16)
+    t0 = time.perf_counter()
+    operm.gather(x, p.perm[:rows])
+    t_perm = time.perf_counter() - t0
+    return {
+        "value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"fp64 window attention of {done} (window, head) pairs of the {w.name} "
+                  f"{'regular' if method == 0 else 'shifted'} layout ({flops / 1e9:.1f} GFLOP in {t_attn:.1f} s); "
+                  f"planner {t_plan:.2f} s for the whole grid; gather {2 * rows * w.heads * D * 2 / t_perm / 1e9:.2f} "
+                  f"GB/s on {rows} rows",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the path has no multi-GPU mode (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import window_attention_amd as wa
+    from window_attention_amd.workloads import BY_NAME
+    w = BY_NAME[args.workload]
+    dev = "cuda"
+    wa.load_library()
+    log(f"[bench] {w.name}: grid {w.T}x{w.H}x{w.W} B={w.batch} heads={w.heads} D={w.head_dim} "
+        f"entry={w.entry} schedule={','.join(w.schedule)}")
+    st = Step(w, wa, torch, dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    # whole-step timing, no per-kernel events inside
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        st.run()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step")
+    # per-kernel timing pass (events around every launch, same stream)
+    for _ in range(args.steps):
+        st.run(timed=True)
+    torch.cuda.synchronize()
+    attn_ms = [a.elapsed_time(b) for a, b in st.attn_events]
+    perm_ms = [a.elapsed_time(b) for a, b in st.perm_events]
+    nl = len(w.schedule)
+    attn_flops_step = sum(st.attn_flops)
+    attn_ms_step = sum(attn_ms) / args.steps
+    perm_ms_step = sum(perm_ms) / args.steps
+    attn_tfs = attn_flops_step / (attn_ms_step * 1e-3) / 1e12
+    perm_bytes_launch = st.perm_bytes_data
+    perm_gbs = perm_bytes_launch / (sum(perm_ms) / len(perm_ms) * 1e-3) / 1e9
+    for li, lay in enumerate(w.schedule):
+        ms = sorted(attn_ms[li::nl])[len(attn_ms[li::nl]) // 2]
+        log(f"[bench] attn layer {li} ({lay}): median {ms:.3f} ms, {st.attn_flops[li] / ms / 1e9:.1f} TFLOP/s")
+    log(f"[bench] permutes: {len(perm_ms) // args.steps}/step, mean {sum(perm_ms) / len(perm_ms) * 1e3:.1f} us, "
+        f"{perm_gbs:.0f} GB/s")
+    value = attn_flops_step / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "window-attn useful TFLOP/s + permute GB/s, 21x45x80 grid bf16, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "grid": [w.T, w.H, w.W], "window_counts": [w.nt, w.nh, w.nw],
+                   "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "entry": w.entry,
+                   "schedule": ",".join(w.schedule), "parallelism": "none (1 GPU)"},
+        "attn_tflops": round(attn_tfs, 2),
+        "permute_gbps": round(perm_gbs, 1),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tfs, 2), "peak": BF16_MFMA_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(attn_tfs / BF16_MFMA_PEAK_TFS, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel<128,4>",
+                     "avg_launch_ms": round(attn_ms_step / nl, 4),
+                     "flops_per_launch": attn_flops_step / nl},
+        "roofline_permute": {"bound": "hbm", "achieved": round(perm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(perm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                             "kernel": "permute_rows_kernel",
+                             "avg_launch_ms": round(sum(perm_ms) / len(perm_ms), 4),
+                             "bytes_per_launch": perm_bytes_launch},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle sample, about {args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

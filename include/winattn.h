@@ -1,0 +1,169 @@
+/*
+ * winattn.h -- C ABI of the MI355X (gfx950) 3D window-attention library.
+ *
+ * The operations follow the page "Window-Aligned Sequence Parallelism
+ * (SeedVR2)" (vLLM-Omni design notes):
+ *   - win_plan        section "Window layouts": 720p-normalised window sizes,
+ *                     regular and half-window-shifted clipped windows,
+ *                     w-outermost / t-innermost enumeration, row-major tokens
+ *                     inside a window, canonical id (t*H + h)*W + w, ragged
+ *                     windows described by cu_seqlens.
+ *   - win_permute     section "SeedVR2 integration": entry distribution of
+ *                     canonical rows into window order and final
+ *                     reconstruction back to canonical order.
+ *   - win_transition  sections "Motivation" and "Plan A redistribution": the
+ *                     layout change between consecutive layers, a local
+ *                     permutation of rows on one device, done in one pass.
+ *   - win_attn_fwd    sections "Motivation" and "SeedVR2 integration":
+ *                     attention only inside each window, one packed
+ *                     variable-length call over cu_seqlens segments.
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns WIN_OK (0) or a negative status; win_strerror()
+ *     names it.  Arguments are validated on the host before anything is
+ *     launched; on a non-zero status nothing has been enqueued.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no pointer after a call returns.
+ *   - "device" pointers are HIP device allocations of the current device;
+ *     "host" pointers are ordinary process memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Device work is
+ *     enqueued on it asynchronously; no function synchronises the device.
+ *   - Token tensors are contiguous [B, L, row] with a 16-byte aligned base;
+ *     the same plan applies to every batch element.  Attention tensors are
+ *     [B, L, heads, head_dim] bf16.
+ *   - Sources and destinations must not overlap (WIN_EINVAL if src == dst).
+ */
+#ifndef WINATTN_H
+#define WINATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define WIN_OK            0
+#define WIN_EINVAL       (-1) /* bad argument, geometry, null/aliased pointer */
+#define WIN_EUNSUPPORTED (-2) /* dtype, head_dim, row size or alignment not handled */
+#define WIN_EOVERFLOW    (-3) /* a size or index exceeds the 32-bit index range */
+#define WIN_EDEVICE      (-4) /* the HIP runtime reported an error */
+
+/* ---- enumerations -------------------------------------------------------- */
+#define WIN_METHOD_REGULAR 0 /* slice(k*w, min((k+1)*w, n)) on every axis */
+#define WIN_METHOD_SHIFTED 1 /* every cut moved by half a window, clipped to [0, n] */
+
+#define WIN_DTYPE_BF16 0 /* 2-byte elements */
+#define WIN_DTYPE_FP16 1 /* 2-byte elements */
+#define WIN_DTYPE_FP32 2 /* 4-byte elements */
+
+#define WIN_GATHER  0 /* dst[b, j] = src[b, idx[j]]   canonical -> window order */
+#define WIN_SCATTER 1 /* dst[b, idx[j]] = src[b, j]   window -> canonical order */
+
+/* ---- win_plan ------------------------------------------------------------ */
+typedef struct win_plan_info {
+    int32_t wt, wh, ww;             /* window extent on t, h, w */
+    int32_t segs_t, segs_h, segs_w; /* number of window segments on each axis */
+    int32_t num_windows;            /* N = segs_t * segs_h * segs_w */
+    int32_t max_seqlen;             /* tokens in the largest window */
+    int64_t num_tokens;             /* L = T * H * W */
+} win_plan_info;
+
+/*
+ * Window layout of a post-patch (T, H, W) token grid (page section "Window
+ * layouts").
+ *
+ * Sizes: scale = sqrt(45*80 / (H*W)) in IEEE double, wh = ceil(round(H*scale)
+ * / nh), ww = ceil(round(W*scale) / nw), wt = ceil(min(T, 30) / nt), with
+ * round-half-to-even on the double product.
+ * Axis segments (extent n, window w): regular [k*w, min((k+1)*w, n));
+ * shifted: if w >= n the single segment [0, n), otherwise the cuts are 0,
+ * floor(w/2), floor(w/2) + w, ... clipped to n, empty segments dropped.
+ * Windows are the products of axis segments, enumerated w outermost, then h,
+ * then t; tokens inside a window are row-major in (t, h, w).
+ *
+ * Arguments
+ *   T, H, W, nt, nh, nw  > 0; T*H*W must be < 2^31.
+ *   method               WIN_METHOD_REGULAR or WIN_METHOD_SHIFTED.
+ *   info                 host, required: receives sizes and counts.
+ *   perm                 [L] int32: perm[j] = canonical id at window position j.
+ *   inv                  [L] int32: inv[perm[j]] = j.
+ *   cu_seqlens           [N+1] int32 prefix sums of window sizes (cu[0] = 0).
+ *   boxes                [N*6] int32: (t0, t1, h0, h1, w0, w1) per window.
+ *   Any of perm / inv / cu_seqlens / boxes may be NULL (not written), so a
+ *   first call with all four NULL is a size query.
+ *   on_device            0: the four tables are host memory, filled on the
+ *                        host before return.  1: they are device memory,
+ *                        filled by a kernel enqueued on `stream`.
+ * Errors: WIN_EINVAL (non-positive input, rescaled extent of zero, bad
+ * method, info NULL), WIN_EOVERFLOW (L >= 2^31), WIN_EDEVICE.
+ */
+int win_plan(int32_t T, int32_t H, int32_t W, int32_t nt, int32_t nh, int32_t nw, int32_t method,
+             win_plan_info* info, int32_t* perm, int32_t* inv, int32_t* cu_seqlens, int32_t* boxes,
+             int32_t on_device, void* stream);
+
+/*
+ * Entry gather / exit scatter of whole token rows (page section "SeedVR2
+ * integration": entry distribution and final reconstruction).
+ *   mode WIN_GATHER:  dst[b, j, :] = src[b, idx[j], :]
+ *   mode WIN_SCATTER: dst[b, idx[j], :] = src[b, j, :]
+ *   src, dst   device, [batch, L, row_elems] of `dtype`, 16-byte aligned, no overlap.
+ *   idx        device, [L] int32, a permutation of 0..L-1 (win_plan's perm).
+ *              Entries outside [0, L) are clamped into range, so no access
+ *              leaves the tensors; the rows they touch are then unspecified.
+ *   row_elems * element size must be a multiple of 16 bytes.  With L == 0
+ *   nothing is read or written and the pointers may be NULL.
+ * Bit-exact copy.  Errors: WIN_EINVAL, WIN_EUNSUPPORTED (dtype, row size,
+ * alignment), WIN_EOVERFLOW (batch*L*row_bytes/16 >= 2^32), WIN_EDEVICE.
+ */
+int win_permute(const void* src, void* dst, const int32_t* idx, int64_t L, int32_t batch, int64_t row_elems,
+                int32_t dtype, int32_t mode, void* stream);
+
+/*
+ * Layout transition A -> B in one pass (page sections "Motivation" and "Plan A
+ * redistribution": on one device a local permutation of rows):
+ *   dst[b, j, :] = src[b, inv_src[perm_dst[j]], :]
+ * inv_src is layout A's inv and perm_dst is layout B's perm (device, [L]
+ * int32 each, clamped into range as in win_permute).  Other arguments and
+ * errors as in win_permute.
+ */
+int win_transition(const void* src, void* dst, const int32_t* inv_src, const int32_t* perm_dst, int64_t L,
+                   int32_t batch, int64_t row_elems, int32_t dtype, void* stream);
+
+/*
+ * Variable-length window attention, forward (page sections "Motivation" and
+ * "SeedVR2 integration"): for every batch element b, window i (rows
+ * cu_seqlens[i] .. cu_seqlens[i+1]-1) and head h,
+ *   O = softmax(Q K^T * softmax_scale) V      (no mask inside a window)
+ *   lse = rowmax + log(rowsum)                 (natural log, per query row)
+ * q, k, v, o   device, bf16 [batch, L, heads, head_dim], window-ordered,
+ *              16-byte aligned; o must not overlap q, k or v.
+ * lse          device fp32 [batch, heads, L] or NULL (not written).
+ * cu_seqlens   device int32 [num_windows + 1], non-decreasing, cu[0] >= 0,
+ *              cu[num_windows] <= L; zero-length windows are allowed; every
+ *              window must hold at most max_seqlen rows.  Entries that break
+ *              these rules are clamped so that no access leaves the tensors;
+ *              the rows involved are then unspecified.  Rows outside every
+ *              window are not written.
+ * head_dim     64 or 128.  softmax_scale > 0 (1/sqrt(head_dim) is the usual).
+ * Arithmetic: bf16 inputs, fp32 MFMA accumulation and fp32 online softmax,
+ * bf16 output rounded to nearest even.  Deterministic: no atomics, a fixed
+ * reduction order per output row, independent of batch size and grid.
+ * Errors: WIN_EINVAL, WIN_EUNSUPPORTED (head_dim, alignment), WIN_EOVERFLOW,
+ * WIN_EDEVICE.
+ */
+int win_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+                 int32_t num_windows, int32_t max_seqlen, int64_t L, int32_t batch, int32_t heads,
+                 int32_t head_dim, float softmax_scale, void* stream);
+
+/* Static string naming a status code. */
+const char* win_strerror(int status);
+
+/* Static string naming the build: target arch, kernel variants and tiles. */
+const char* win_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WINATTN_H */

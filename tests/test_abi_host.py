@@ -1,0 +1,148 @@
+"""C ABI on the host: the library loads, exports every declared symbol, the
+host planner matches the oracle bit for bit, and bad arguments are rejected
+before anything is launched.  No GPU needed."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import window_attention_amd as wa
+from oracle import plan as oplan
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "winattn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s+(win_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = wa.load_library()
+    names = _declared_functions()
+    assert set(names) >= {"win_plan", "win_permute", "win_transition", "win_attn_fwd", "win_strerror",
+                          "win_build_info"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {wa.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported"
+
+
+def test_status_strings_and_build_info():
+    lib = wa.load_library()
+    for code in (0, -1, -2, -3, -4):
+        assert lib.win_strerror(code).decode() != "unknown status"
+    assert lib.win_strerror(-99).decode() == "unknown status"
+    assert "gfx950" in wa.build_info()
+
+
+def _host_plan(T, H, W, nt, nh, nw, method):
+    p = wa.plan(T, H, W, nt, nh, nw, method)
+    return p
+
+
+def _compare(T, H, W, nt, nh, nw, method):
+    o = oplan.plan(T, H, W, nt, nh, nw, method)
+    p = _host_plan(T, H, W, nt, nh, nw, method)
+    assert (p.wt, p.wh, p.ww) == (o.wt, o.wh, o.ww)
+    assert p.num_windows == o.num_windows and p.max_seqlen == o.max_seqlen and p.num_tokens == T * H * W
+    assert p.segs == (len(oplan.axis_segments(T, o.wt, method)), len(oplan.axis_segments(H, o.wh, method)),
+                      len(oplan.axis_segments(W, o.ww, method)))
+    assert np.array_equal(p.perm.numpy(), np.asarray(o.perm, dtype=np.int32))
+    assert np.array_equal(p.inv.numpy(), np.asarray(o.inv, dtype=np.int32))
+    assert np.array_equal(p.cu_seqlens.numpy(), np.asarray(o.cu_seqlens, dtype=np.int32))
+    assert np.array_equal(p.boxes.numpy(), np.asarray(o.boxes, dtype=np.int32).reshape(-1, 6))
+
+
+_NS = (1, 2, 3, 5, 9, 17, 33, 65, 129)
+
+
+@pytest.mark.parametrize("grid", [(1, 3, 4), (2, 5, 7), (3, 6, 6), (5, 9, 16), (6, 11, 5), (7, 4, 13), (31, 3, 2)])
+@pytest.mark.parametrize("method", [0, 1])
+def test_host_planner_matches_oracle_sweep(grid, method):
+    for nt, nh, nw in itertools.product((1, 2, 3, 4, 31), _NS, _NS):
+        _compare(*grid, nt, nh, nw, method)
+
+
+@pytest.mark.parametrize("cfg", [(5, 9, 16, 2, 3, 3), (4, 45, 80, 4, 3, 3), (21, 45, 80, 4, 3, 3),
+                                 (21, 68, 120, 4, 3, 3), (9, 9, 64, 2, 3, 5), (3, 3, 192, 1, 2, 7),
+                                 (40, 17, 23, 3, 2, 2)])
+@pytest.mark.parametrize("method", [0, 1])
+def test_host_planner_matches_oracle_workload_grids(cfg, method):
+    _compare(*cfg, method)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("method", [0, 1])
+def test_host_planner_matches_oracle_long_grid(method):
+    _compare(31, 90, 160, 4, 3, 3, method)
+
+
+def _status(*args):
+    lib = wa.load_library()
+    info = wa._PlanInfo()
+    return lib.win_plan(*args[:7], ctypes.byref(info), None, None, None, None, args[7], None)
+
+
+def test_plan_rejects_bad_geometry():
+    assert _status(0, 4, 4, 1, 1, 1, 0, 0) == -1
+    assert _status(4, 4, -4, 1, 1, 1, 0, 0) == -1
+    assert _status(4, 4, 4, 1, 0, 1, 0, 0) == -1
+    assert _status(4, 4, 4, 1, 1, 1, 2, 0) == -1          # unknown method
+    assert _status(4, 4, 4, 1, 1, 1, 0, 2) == -1          # on_device must be 0/1
+    assert _status(2048, 1024, 1024, 1, 1, 1, 0, 0) == -3  # L = 2^31
+    lib = wa.load_library()
+    assert lib.win_plan(4, 4, 4, 1, 1, 1, 0, None, None, None, None, None, 0, None) == -1  # info required
+    assert _status(4, 4, 4, 1, 1, 1, 0, 0) == 0
+
+
+def test_plan_size_query_only():
+    lib = wa.load_library()
+    info = wa._PlanInfo()
+    assert lib.win_plan(21, 45, 80, 4, 3, 3, 1, ctypes.byref(info), None, None, None, None, 0, None) == 0
+    assert (info.wt, info.wh, info.ww, info.num_windows, info.max_seqlen, info.num_tokens) == \
+        (6, 15, 27, 64, 2430, 75600)
+
+
+def test_device_entry_points_validate_before_launch():
+    lib = wa.load_library()
+    A = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
+    B = ctypes.c_void_p(0x20000)
+    M = ctypes.c_void_p(0x10008)   # misaligned
+    I = ctypes.c_void_p(0x30000)
+    # permute
+    assert lib.win_permute(None, B, I, 10, 1, 64, 0, 0, None) == -1
+    assert lib.win_permute(A, B, None, 10, 1, 64, 0, 0, None) == -1
+    assert lib.win_permute(A, B, I, 10, 1, 64, 9, 0, None) == -2     # dtype
+    assert lib.win_permute(M, B, I, 10, 1, 64, 0, 0, None) == -2     # alignment
+    assert lib.win_permute(A, B, I, 10, 1, 3, 0, 0, None) == -2      # row not a multiple of 16 bytes
+    assert lib.win_permute(A, A, I, 10, 1, 64, 0, 0, None) == -1     # in place
+    assert lib.win_permute(A, B, I, 10, 1, 64, 0, 7, None) == -1     # mode
+    assert lib.win_permute(A, B, I, 1 << 31, 1, 64, 0, 0, None) == -3
+    assert lib.win_permute(A, B, I, -1, 1, 64, 0, 0, None) == -1
+    assert lib.win_permute(A, B, I, 10, 0, 64, 0, 0, None) == -1
+    assert lib.win_permute(A, B, I, 0, 1, 64, 0, 0, None) == 0       # empty: nothing to do
+    assert lib.win_permute(None, None, None, 0, 1, 64, 0, 0, None) == 0
+    # transition
+    assert lib.win_transition(A, B, None, I, 10, 1, 64, 0, None) == -1
+    assert lib.win_transition(A, B, I, None, 10, 1, 64, 0, None) == -1
+    assert lib.win_transition(A, A, I, I, 10, 1, 64, 0, None) == -1
+    # attention
+    f = ctypes.c_float
+    C = ctypes.c_void_p(0x40000)
+    O = ctypes.c_void_p(0x1000000)
+    assert lib.win_attn_fwd(None, A, B, O, None, I, 1, 8, 8, 1, 1, 128, f(0.1), None) == -1
+    assert lib.win_attn_fwd(A, A, A, O, None, None, 1, 8, 8, 1, 1, 128, f(0.1), None) == -1
+    assert lib.win_attn_fwd(A, A, A, O, None, I, 1, 8, 8, 1, 1, 96, f(0.1), None) == -2   # head_dim
+    assert lib.win_attn_fwd(A, A, A, O, None, I, 1, 8, 8, 1, 1, 128, f(0.0), None) == -1  # scale
+    assert lib.win_attn_fwd(A, A, A, O, None, I, 1, 8, 8, 1, 1, 128, f(float("nan")), None) == -1
+    assert lib.win_attn_fwd(M, A, A, O, None, I, 1, 8, 8, 1, 1, 128, f(0.1), None) == -2
+    assert lib.win_attn_fwd(A, B, C, A, None, I, 1, 8, 8, 1, 1, 128, f(0.1), None) == -1  # o aliases q
+    assert lib.win_attn_fwd(A, B, C, O, None, I, 1, 9, 8, 1, 1, 128, f(0.1), None) == -1  # max_seqlen > L
+    assert lib.win_attn_fwd(A, B, C, O, None, I, -1, 8, 8, 1, 1, 128, f(0.1), None) == -1
+    assert lib.win_attn_fwd(A, B, C, O, None, I, 1, 8, 1 << 31, 1, 1, 128, f(0.1), None) == -3
+    assert lib.win_attn_fwd(A, B, C, O, None, I, 0, 0, 8, 1, 1, 128, f(0.1), None) == 0   # no windows

@@ -1,0 +1,213 @@
+"""win_attn_fwd against the fp64 oracle (GPU).
+
+Small cases are compared element by element over every output; the full-size
+workloads are run in the same launch configuration the benchmark times and
+compared on sampled (batch, window, head) blocks that the oracle computes one
+by one, choosing the largest, smallest and edge windows."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import window_attention_amd as wa
+from oracle import attention as oatt
+from oracle import permute as operm
+from oracle import plan as oplan
+from tests.gpu_helpers import LSE_ABS, MAX_ABS, MEAN_ABS, assert_close_full, check_window_head, method_of, say, \
+    to_f64
+from window_attention_amd.inputs import normal, qkv
+from window_attention_amd.workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _cu(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("lengths", [
+    [1, 39, 64, 65, 127, 128, 129, 200],      # single token, sub-tile, tile edges, multi-tile ragged tails
+    [300, 0, 0, 257, 5],                      # empty segments in the middle
+    [700],                                    # several key tiles and query tiles, ragged tail
+])
+def test_ragged_segments_full_compare(D, lengths):
+    say(f"ragged D={D} lengths={lengths}")
+    cu = _cu(lengths)
+    L, B, Hh = int(cu[-1]), 2, 3
+    q, k, v = (normal((B, L, Hh, D), 500 + t, device=DEV) for t in range(3))
+    o, lse = wa.attn_fwd(q, k, v, torch.as_tensor(cu, device=DEV), max(lengths), return_lse=True)
+    ref_o, ref_lse = oatt.window_attention(to_f64(q), to_f64(k), to_f64(v), cu)
+    assert_close_full(o, lse, ref_o, ref_lse)
+
+
+def test_rows_outside_windows_untouched_and_empty_plan():
+    D, Hh, L = 128, 2, 96
+    q, k, v = (normal((1, L, Hh, D), 600 + t, device=DEV) for t in range(3))
+    cu = torch.tensor([0, 40, 70], dtype=torch.int32, device=DEV)
+    out = torch.full_like(q, 7.0)
+    lse = wa.attn_fwd(q, k, v, cu, 40, out=out, return_lse=True)[1]
+    assert torch.all(out[:, 70:] == 7.0)
+    ref_o, ref_lse = oatt.window_attention(to_f64(q), to_f64(k), to_f64(v), [0, 40, 70])
+    assert_close_full(out[:, :70], lse[:, :, :70], ref_o[:, :70], ref_lse[:, :, :70])
+    # no windows at all: nothing is written
+    out2 = torch.full_like(q, 3.0)
+    wa.attn_fwd(q, k, v, torch.zeros(1, dtype=torch.int32, device=DEV), 0, out=out2)
+    torch.cuda.synchronize()
+    assert torch.all(out2 == 3.0)
+
+
+def test_closed_forms_on_device():
+    # Q = 0: every row is its window's mean of V; LSE = log(n)
+    D, Hh = 128, 2
+    lengths = [5, 77, 130]
+    cu = _cu(lengths)
+    L = int(cu[-1])
+    q = torch.zeros((1, L, Hh, D), dtype=torch.bfloat16, device=DEV)
+    k, v = (normal((1, L, Hh, D), 700 + t, device=DEV) for t in range(2))
+    o, lse = wa.attn_fwd(q, k, v, torch.as_tensor(cu, device=DEV), max(lengths), return_lse=True)
+    vh = to_f64(v)
+    for i, n in enumerate(lengths):
+        a, e = cu[i], cu[i + 1]
+        mean = vh[:, a:e].mean(axis=1, keepdims=True)
+        assert np.max(np.abs(to_f64(o[:, a:e]) - mean)) <= MAX_ABS
+        assert np.max(np.abs(lse[:, :, a:e].cpu().numpy() - math.log(n))) <= LSE_ABS
+
+
+@pytest.mark.parametrize("method", [0, 1])
+def test_tiny_clip_both_layouts(method):
+    """5x9x16 grid, 1 head x 64, fp32 draws cast to bf16 on the device; the
+    oracle runs on exactly the bf16 values; outputs compared in canonical
+    order against the masked brute force as well."""
+    w = WORKLOADS[0]
+    qf, kf, vf = qkv(w.wid, 1, w.L, w.heads, w.head_dim, device=DEV, dtype=torch.float32)
+    q, k, v = (x.to(torch.bfloat16) for x in (qf, kf, vf))
+    p = wa.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, method, device=DEV)
+    qw, kw, vw = (wa.gather(x, p.perm) for x in (q, k, v))
+    ow, lse = wa.attn_fwd(qw, kw, vw, p.cu_seqlens, p.max_seqlen, return_lse=True)
+    o = wa.scatter(ow, p.perm)
+    op = oplan.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, method)
+    win = np.repeat(np.arange(op.num_windows), np.diff(op.cu_seqlens))[np.asarray(op.inv)]
+    ref_o, ref_lse = oatt.masked_full_attention(to_f64(q), to_f64(k), to_f64(v), win)
+    assert_close_full(o, lse[:, :, p.inv.long()], ref_o, ref_lse)
+
+
+def test_clip_720p_full_compare():
+    """4x45x80 clip, 24 heads x 128, regular layout: every output compared."""
+    w = WORKLOADS[1]
+    say(f"full compare {w.name}")
+    q, k, v = qkv(w.wid, w.batch, w.L, w.heads, w.head_dim, w.sigma, device=DEV)
+    p = wa.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, 0, device=DEV)
+    qw, kw, vw = (wa.gather(x, p.perm) for x in (q, k, v))
+    ow, lse = wa.attn_fwd(qw, kw, vw, p.cu_seqlens, p.max_seqlen, return_lse=True)
+    o = wa.scatter(ow, p.perm)
+    op = oplan.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, 0)
+    ref_w, ref_lse = oatt.window_attention(operm.gather(to_f64(q), op.perm), operm.gather(to_f64(k), op.perm),
+                                           operm.gather(to_f64(v), op.perm), op.cu_seqlens)
+    assert_close_full(o, None, operm.scatter(ref_w, op.perm), None)
+    assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ABS
+
+
+def _sample_windows(cu, rng, extra=2):
+    sizes = np.diff(cu)
+    nz = np.nonzero(sizes)[0]
+    pick = {int(nz[0]), int(nz[-1]), int(nz[np.argmax(sizes[nz])]), int(nz[np.argmin(sizes[nz])])}
+    pick.update(int(x) for x in rng.choice(nz, size=min(extra, len(nz)), replace=False))
+    return sorted(pick)
+
+
+def _run_chain(w, q, k, v):
+    """The benchmark's step: gather into the entry layout, then per layer a
+    fused transition when the layout changes and window attention; returns
+    per-layer (layout, carried q/k/v, o, lse, plan)."""
+    plans = {m: wa.plan_cached(w.T, w.H, w.W, w.nt, w.nh, w.nw, method_of(m), device=DEV) for m in "RS"}
+    cur = w.entry
+    qw, kw, vw = (wa.gather(x, plans[cur].perm) for x in (q, k, v))
+    layers = []
+    for lay in w.schedule:
+        if lay != cur:
+            qw, kw, vw = (wa.transition(x, plans[cur].inv, plans[lay].perm) for x in (qw, kw, vw))
+            cur = lay
+        p = plans[lay]
+        o, lse = wa.attn_fwd(qw, kw, vw, p.cu_seqlens, p.max_seqlen, return_lse=True)
+        layers.append((lay, (qw, kw, vw), o, lse, p))
+    return layers
+
+
+@pytest.mark.parametrize("wi", [2, 3, 4])
+def test_full_size_workloads_sampled(wi):
+    w = WORKLOADS[wi]
+    q, k, v = qkv(w.wid, w.batch, w.L, w.heads, w.head_dim, w.sigma, device=DEV)
+    layers = _run_chain(w, q, k, v)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(100 + wi)
+    for li, (lay, (qw, kw, vw), o, lse, p) in enumerate(layers):
+        op = oplan.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, method_of(lay))
+        # the carried tensors are the canonical tensors in this layout, bit for bit (sampled rows vs oracle perm)
+        rows = np.unique(rng.integers(0, w.L, 2000))
+        for x_can, x_lay in ((q, qw), (k, kw), (v, vw)):
+            got = x_lay[:, torch.as_tensor(rows, device=DEV)]
+            want = x_can[:, torch.as_tensor(np.asarray(op.perm)[rows], device=DEV)]
+            assert torch.equal(got, want)
+        cu = np.asarray(op.cu_seqlens)
+        worst = (0.0, 0.0, 0.0)
+        for b in range(w.batch):
+            for i in _sample_windows(cu, rng):
+                for h in sorted({0, w.heads - 1, int(rng.integers(0, w.heads))}):
+                    mx, mean, lerr, n = check_window_head(qw, kw, vw, o, lse, cu, b, i, h)
+                    assert mx <= MAX_ABS and mean <= MEAN_ABS and lerr <= LSE_ABS, (w.name, li, b, i, h, n, mx,
+                                                                                     mean, lerr)
+                    worst = tuple(max(a, c) for a, c in zip(worst, (mx, mean, lerr)))
+        say(f"{w.name} layer {li} ({lay}): worst max={worst[0]:.3e} mean={worst[1]:.3e} lse={worst[2]:.3e}")
+
+
+def test_batch_invariance_hd_grid():
+    """Element 1 of the B=2 run of the 21x68x120 grid equals a B=1 run on the
+    same draws, bit for bit, in both layouts."""
+    w = WORKLOADS[3]
+    q, k, v = qkv(w.wid, 2, w.L, w.heads, w.head_dim, w.sigma, device=DEV)
+    q1, k1, v1 = qkv(w.wid, 1, w.L, w.heads, w.head_dim, w.sigma, device=DEV, batch_offset=1)
+    assert torch.equal(q1[0], q[1]) and torch.equal(v1[0], v[1])
+    for m in (0, 1):
+        p = wa.plan_cached(w.T, w.H, w.W, w.nt, w.nh, w.nw, m, device=DEV)
+        o2 = wa.attn_fwd(wa.gather(q, p.perm), wa.gather(k, p.perm), wa.gather(v, p.perm), p.cu_seqlens,
+                         p.max_seqlen)
+        o1 = wa.attn_fwd(wa.gather(q1, p.perm), wa.gather(k1, p.perm), wa.gather(v1, p.perm), p.cu_seqlens,
+                         p.max_seqlen)
+        assert torch.equal(o2[1], o1[0])
+
+
+def test_isolation_and_determinism():
+    """Change every token of one window: every other window's output is
+    bit-identical; repeated runs are bit-identical."""
+    w = WORKLOADS[1]
+    q, k, v = qkv(w.wid, 1, w.L, w.heads, w.head_dim, device=DEV)
+    p = wa.plan_cached(w.T, w.H, w.W, w.nt, w.nh, w.nw, 1, device=DEV)
+    qw, kw, vw = (wa.gather(x, p.perm) for x in (q, k, v))
+    o = wa.attn_fwd(qw, kw, vw, p.cu_seqlens, p.max_seqlen)
+    o_again = wa.attn_fwd(qw, kw, vw, p.cu_seqlens, p.max_seqlen)
+    assert torch.equal(o, o_again)
+    cu = p.cu_seqlens.cpu().numpy()
+    i = 5
+    a, e = int(cu[i]), int(cu[i + 1])
+    q2, k2, v2 = qw.clone(), kw.clone(), vw.clone()
+    for x in (q2, k2, v2):
+        x[:, a:e] = -x[:, a:e] * 0.5
+    o2 = wa.attn_fwd(q2, k2, v2, p.cu_seqlens, p.max_seqlen)
+    assert torch.equal(o2[:, :a], o[:, :a]) and torch.equal(o2[:, e:], o[:, e:])
+    assert not torch.equal(o2[:, a:e], o[:, a:e])
+
+
+def test_argument_errors():
+    q = torch.zeros((1, 8, 1, 96), dtype=torch.bfloat16, device=DEV)
+    cu = torch.tensor([0, 8], dtype=torch.int32, device=DEV)
+    with pytest.raises(wa.WinAttnError):
+        wa.attn_fwd(q, q, q, cu, 8)            # head_dim 96
+    q = torch.zeros((1, 8, 1, 128), dtype=torch.float16, device=DEV)
+    with pytest.raises(wa.WinAttnError):
+        wa.attn_fwd(q, q, q, cu, 8)            # fp16 inputs
+    q = torch.zeros((1, 8, 1, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(wa.WinAttnError):
+        wa.attn_fwd(q, q, q, cu, 8, out=q)     # output aliases the inputs

@@ -1,0 +1,255 @@
+"""MI355X (gfx950) 3D window attention: Python binding of ``libwinattn.so``.
+
+Argument marshalling only: every step runs in the library's HIP kernels (or,
+for ``plan(..., device=None)``, its host planner).  PyTorch supplies device
+memory and the current stream.  The C entry points are documented in
+``include/winattn.h``; their names are kept here:
+
+    plan()        -> win_plan
+    gather()      -> win_permute(mode=WIN_GATHER)
+    scatter()     -> win_permute(mode=WIN_SCATTER)
+    transition()  -> win_transition
+    attn_fwd()    -> win_attn_fwd
+
+If the library has not been built the first call raises ``WinAttnError``;
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from collections import OrderedDict
+from dataclasses import dataclass
+
+__all__ = ["WinAttnError", "Plan", "plan", "plan_cached", "gather", "scatter", "transition", "attn_fwd",
+           "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
+
+REGULAR = 0
+SHIFTED = 1
+_DTYPES = {}  # torch dtype -> WIN_DTYPE_*, filled lazily
+_GATHER, _SCATTER = 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwinattn.so")
+_lib = None
+
+
+class WinAttnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        msg = what
+        if _lib is not None and code < 0:
+            msg = f"{what}: {_lib.win_strerror(code).decode()} (status {code})"
+        super().__init__(msg)
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [("wt", ctypes.c_int32), ("wh", ctypes.c_int32), ("ww", ctypes.c_int32),
+                ("segs_t", ctypes.c_int32), ("segs_h", ctypes.c_int32), ("segs_w", ctypes.c_int32),
+                ("num_windows", ctypes.c_int32), ("max_seqlen", ctypes.c_int32), ("num_tokens", ctypes.c_int64)]
+
+
+def load_library():
+    """Load ``libwinattn.so`` (built in-tree by ``window_attention_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise WinAttnError(-4, f"{LIB_PATH} is missing: build it with 'python -m window_attention_amd.build'")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    lib.win_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_PlanInfo), vp, vp, vp, vp, i32, vp]
+    lib.win_plan.restype = ctypes.c_int
+    lib.win_permute.argtypes = [vp, vp, vp, i64, i32, i64, i32, i32, vp]
+    lib.win_permute.restype = ctypes.c_int
+    lib.win_transition.argtypes = [vp, vp, vp, vp, i64, i32, i64, i32, vp]
+    lib.win_transition.restype = ctypes.c_int
+    lib.win_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, vp]
+    lib.win_attn_fwd.restype = ctypes.c_int
+    lib.win_strerror.argtypes = [ctypes.c_int]
+    lib.win_strerror.restype = ctypes.c_char_p
+    lib.win_build_info.argtypes = []
+    lib.win_build_info.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def build_info() -> str:
+    return load_library().win_build_info().decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise WinAttnError(status, what)
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dtype_code(t):
+    import torch
+    if not _DTYPES:
+        _DTYPES.update({torch.bfloat16: 0, torch.float16: 1, torch.float32: 2})
+    if t.dtype not in _DTYPES:
+        raise WinAttnError(-2, f"dtype {t.dtype} is not supported")
+    return _DTYPES[t.dtype]
+
+
+def _require_cuda(name, t, dtype=None):
+    if not t.is_cuda:
+        raise WinAttnError(-1, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise WinAttnError(-1, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise WinAttnError(-2, f"{name} must be {dtype}, got {t.dtype}")
+
+
+@dataclass
+class Plan:
+    """Tables of one window layout (see ``win_plan`` in include/winattn.h)."""
+    T: int
+    H: int
+    W: int
+    method: int
+    wt: int
+    wh: int
+    ww: int
+    segs: tuple
+    num_windows: int
+    max_seqlen: int
+    num_tokens: int
+    perm: object        # torch.int32 [L]
+    inv: object         # torch.int32 [L]
+    cu_seqlens: object  # torch.int32 [N+1]
+    boxes: object       # torch.int32 [N, 6]
+
+
+def plan(T, H, W, nt, nh, nw, method=REGULAR, device=None) -> Plan:
+    """Window layout tables.  ``device=None`` fills host (CPU) tensors with the
+    host planner; a CUDA device fills device tensors with the device kernel on
+    the current stream."""
+    import torch
+    lib = load_library()
+    info = _PlanInfo()
+    _check(lib.win_plan(T, H, W, nt, nh, nw, method, ctypes.byref(info), None, None, None, None, 0, None),
+           "win_plan(size query)")
+    L, N = info.num_tokens, info.num_windows
+    dev = torch.device("cpu") if device is None else torch.device(device)
+    on_dev = dev.type == "cuda"
+    perm = torch.empty(L, dtype=torch.int32, device=dev)
+    inv = torch.empty(L, dtype=torch.int32, device=dev)
+    cu = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    boxes = torch.empty((N, 6), dtype=torch.int32, device=dev)
+    stream = _stream(perm) if on_dev else None
+    _check(lib.win_plan(T, H, W, nt, nh, nw, method, ctypes.byref(info), _ptr(perm), _ptr(inv), _ptr(cu),
+                        _ptr(boxes), 1 if on_dev else 0, stream), "win_plan")
+    return Plan(T, H, W, method, info.wt, info.wh, info.ww, (info.segs_t, info.segs_h, info.segs_w),
+                N, info.max_seqlen, L, perm, inv, cu, boxes)
+
+
+_PLAN_CACHE: "OrderedDict[tuple, Plan]" = OrderedDict()
+PLAN_CACHE_SIZE = 32
+
+
+def plan_cached(T, H, W, nt, nh, nw, method=REGULAR, device=None) -> Plan:
+    """``plan`` behind an LRU cache keyed on the grid, the window counts, the
+    method and the device (a plan is a pure function of these)."""
+    import torch
+    dev = None if device is None else str(torch.device(device))
+    key = (T, H, W, nt, nh, nw, method, dev)
+    p = _PLAN_CACHE.get(key)
+    if p is not None:
+        _PLAN_CACHE.move_to_end(key)
+        return p
+    p = plan(T, H, W, nt, nh, nw, method, device)
+    _PLAN_CACHE[key] = p
+    while len(_PLAN_CACHE) > PLAN_CACHE_SIZE:
+        _PLAN_CACHE.popitem(last=False)
+    return p
+
+
+def _rows(x):
+    if x.dim() < 2:
+        raise WinAttnError(-1, "token tensors are [B, L, ...]")
+    B, L = x.shape[0], x.shape[1]
+    return B, L, math.prod(x.shape[2:])
+
+
+def _permute(src, idx, mode, out):
+    import torch
+    lib = load_library()
+    _require_cuda("src", src)
+    _require_cuda("idx", idx, torch.int32)
+    B, L, row = _rows(src)
+    if idx.numel() != L:
+        raise WinAttnError(-1, f"index has {idx.numel()} entries, expected L={L}")
+    if out is None:
+        out = torch.empty_like(src)
+    _require_cuda("out", out, src.dtype)
+    if out.shape != src.shape:
+        raise WinAttnError(-1, "out must have the shape of src")
+    _check(lib.win_permute(_ptr(src), _ptr(out), _ptr(idx), L, B, row, _dtype_code(src), mode, _stream(src)),
+           "win_permute")
+    return out
+
+
+def gather(src, perm, out=None):
+    """Canonical -> window order: ``out[b, j] = src[b, perm[j]]``."""
+    return _permute(src, perm, _GATHER, out)
+
+
+def scatter(src, perm, out=None):
+    """Window -> canonical order: ``out[b, perm[j]] = src[b, j]``."""
+    return _permute(src, perm, _SCATTER, out)
+
+
+def transition(src, inv_src, perm_dst, out=None):
+    """Layout A -> layout B in one pass: ``out[b, j] = src[b, inv_src[perm_dst[j]]]``."""
+    import torch
+    lib = load_library()
+    _require_cuda("src", src)
+    _require_cuda("inv_src", inv_src, torch.int32)
+    _require_cuda("perm_dst", perm_dst, torch.int32)
+    B, L, row = _rows(src)
+    if inv_src.numel() != L or perm_dst.numel() != L:
+        raise WinAttnError(-1, "index tables must have L entries")
+    if out is None:
+        out = torch.empty_like(src)
+    _require_cuda("out", out, src.dtype)
+    if out.shape != src.shape:
+        raise WinAttnError(-1, "out must have the shape of src")
+    _check(lib.win_transition(_ptr(src), _ptr(out), _ptr(inv_src), _ptr(perm_dst), L, B, row, _dtype_code(src),
+                              _stream(src)), "win_transition")
+    return out
+
+
+def attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, out=None, return_lse=False):
+    """Window attention over window-ordered bf16 ``[B, L, heads, head_dim]``
+    tensors; windows are the ``cu_seqlens`` segments.  Returns ``out`` or
+    ``(out, lse)`` with ``lse`` fp32 ``[B, heads, L]``."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require_cuda(name, t, torch.bfloat16)
+        if t.dim() != 4 or t.shape != q.shape:
+            raise WinAttnError(-1, f"{name} must be [B, L, heads, head_dim] like q")
+    _require_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    B, L, Hh, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _require_cuda("out", out, torch.bfloat16)
+    if out.shape != q.shape:
+        raise WinAttnError(-1, "out must have the shape of q")
+    lse = torch.empty((B, Hh, L), dtype=torch.float32, device=q.device) if return_lse else None
+    N = cu_seqlens.numel() - 1
+    _check(lib.win_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), N, int(max_seqlen),
+                            L, B, Hh, D, float(softmax_scale), _stream(q)), "win_attn_fwd")
+    return (out, lse) if return_lse else out

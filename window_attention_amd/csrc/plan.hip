@@ -1,0 +1,135 @@
+// win_plan: window sizes, axis segmentation and the integer tables of one
+// layout (page "Window-Aligned Sequence Parallelism (SeedVR2)", section
+// "Window layouts").  Built with -ffp-contract=off: the three double
+// operations of the size formula must round exactly as written.
+#include <cmath>
+
+#include "common.h"
+#include "plan_geometry.h"
+
+namespace winattn {
+namespace {
+
+constexpr int32_t kReferenceArea = 45 * 80;  // 720p post-patch token grid
+constexpr int32_t kMaxTemporalWindow = 30;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// scale = sqrt(45*80 / (H*W)); extent = round-half-even(n * scale).
+int64_t rescaled_extent(int32_t n, int32_t H, int32_t W) {
+    const double scale = std::sqrt((double)kReferenceArea / ((double)H * (double)W));
+    const double x = (double)n * scale;
+    return (int64_t)std::nearbyint(x);  // default rounding mode: to nearest, ties to even
+}
+
+__global__ void fill_tokens_kernel(GridGeom g, int64_t L, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= L) return;
+    const int64_t j = window_position(g, c);
+    if (perm) perm[j] = (int32_t)c;
+    if (inv) inv[c] = (int32_t)j;
+}
+
+__global__ void fill_windows_kernel(GridGeom g, int32_t N, int64_t L, int32_t* __restrict__ cu,
+                                    int32_t* __restrict__ boxes) {
+    const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i > N) return;
+    if (i == N) {
+        if (cu) cu[N] = (int32_t)L;
+        return;
+    }
+    const int32_t st = i % g.t.nseg;
+    const int32_t sh = (i / g.t.nseg) % g.h.nseg;
+    const int32_t sw = i / (g.t.nseg * g.h.nseg);
+    if (cu) cu[i] = (int32_t)window_offset(g, st, sh, sw);
+    if (boxes) {
+        int32_t* bx = boxes + 6 * (int64_t)i;
+        bx[0] = axis_start(g.t, st);
+        bx[1] = axis_end(g.t, st);
+        bx[2] = axis_start(g.h, sh);
+        bx[3] = axis_end(g.h, sh);
+        bx[4] = axis_start(g.w, sw);
+        bx[5] = axis_end(g.w, sw);
+    }
+}
+
+}  // namespace
+}  // namespace winattn
+
+using namespace winattn;
+
+extern "C" int win_plan(int32_t T, int32_t H, int32_t W, int32_t nt, int32_t nh, int32_t nw, int32_t method,
+                        win_plan_info* info, int32_t* perm, int32_t* inv, int32_t* cu_seqlens, int32_t* boxes,
+                        int32_t on_device, void* stream) {
+    if (!info) return WIN_EINVAL;
+    if (T <= 0 || H <= 0 || W <= 0 || nt <= 0 || nh <= 0 || nw <= 0) return WIN_EINVAL;
+    if (method != WIN_METHOD_REGULAR && method != WIN_METHOD_SHIFTED) return WIN_EINVAL;
+    if (on_device != 0 && on_device != 1) return WIN_EINVAL;
+    const int64_t L = (int64_t)T * H * W;
+    if (L >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
+
+    const int64_t rh = rescaled_extent(H, H, W), rw = rescaled_extent(W, H, W);
+    if (rh <= 0 || rw <= 0) return WIN_EINVAL;
+    const int64_t wh = ceil_div(rh, nh), ww = ceil_div(rw, nw);
+    const int64_t wt = ceil_div(T < kMaxTemporalWindow ? T : kMaxTemporalWindow, nt);
+    if (wh >= ((int64_t)1 << 31) || ww >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
+
+    const bool shifted = method == WIN_METHOD_SHIFTED;
+    GridGeom g;
+    g.T = T;
+    g.H = H;
+    g.W = W;
+    g.t = make_axis(T, (int32_t)wt, shifted);
+    g.h = make_axis(H, (int32_t)wh, shifted);
+    g.w = make_axis(W, (int32_t)ww, shifted);
+    const int64_t N = (int64_t)g.t.nseg * g.h.nseg * g.w.nseg;  // <= L
+
+    info->wt = (int32_t)wt;
+    info->wh = (int32_t)wh;
+    info->ww = (int32_t)ww;
+    info->segs_t = g.t.nseg;
+    info->segs_h = g.h.nseg;
+    info->segs_w = g.w.nseg;
+    info->num_windows = (int32_t)N;
+    info->max_seqlen = axis_max_len(g.t) * axis_max_len(g.h) * axis_max_len(g.w);
+    info->num_tokens = L;
+
+    if (!on_device) {
+        for (int64_t c = 0; c < L; ++c) {
+            const int64_t j = window_position(g, c);
+            if (perm) perm[j] = (int32_t)c;
+            if (inv) inv[c] = (int32_t)j;
+        }
+        for (int32_t sw = 0; sw < g.w.nseg; ++sw)
+            for (int32_t sh = 0; sh < g.h.nseg; ++sh)
+                for (int32_t st = 0; st < g.t.nseg; ++st) {
+                    const int32_t i = window_index(g, st, sh, sw);
+                    if (cu_seqlens) cu_seqlens[i] = (int32_t)window_offset(g, st, sh, sw);
+                    if (boxes) {
+                        int32_t* bx = boxes + 6 * (int64_t)i;
+                        bx[0] = axis_start(g.t, st);
+                        bx[1] = axis_end(g.t, st);
+                        bx[2] = axis_start(g.h, sh);
+                        bx[3] = axis_end(g.h, sh);
+                        bx[4] = axis_start(g.w, sw);
+                        bx[5] = axis_end(g.w, sw);
+                    }
+                }
+        if (cu_seqlens) cu_seqlens[N] = (int32_t)L;
+        return WIN_OK;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    constexpr int kThreads = 256;
+    if (perm || inv) {
+        const int64_t blocks = ceil_div(L, kThreads);
+        fill_tokens_kernel<<<dim3((uint32_t)blocks), dim3(kThreads), 0, s>>>(g, L, perm, inv);
+        if (launch_status() != WIN_OK) return WIN_EDEVICE;
+    }
+    if (cu_seqlens || boxes) {
+        const int64_t blocks = ceil_div(N + 1, kThreads);
+        fill_windows_kernel<<<dim3((uint32_t)blocks), dim3(kThreads), 0, s>>>(g, (int32_t)N, L, cu_seqlens, boxes);
+        if (launch_status() != WIN_OK) return WIN_EDEVICE;
+    }
+    return WIN_OK;
+}
