@@ -15,7 +15,11 @@ from window_attention_amd.inputs import bf16_bits
 # tolerance of bf16-in / fp32-accumulate attention against the fp64 oracle
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
-LSE_ABS = 1e-3
+# The kernel's normaliser is the fp32 sum of the probabilities after their
+# round-to-nearest bf16 cast (the weights the P V product uses), each within a
+# relative 2^-9 of the exact value, so the sum is too and its log moves by at
+# most ln(1 + 2^-9) < 2^-9; 5e-4 more covers exp2/log and fp32 accumulation.
+LSE_ABS = 2.0 ** -9 + 5e-4
 
 
 def say(*a):

@@ -44,6 +44,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -79,16 +81,27 @@ struct Layout {
     __device__ static int v_chunk(int r, int c) { return c ^ (kVSwz * (r & 3)); }
 };
 
-__device__ __forceinline__ float wave_xor32(float x) {
-    return __shfl_xor(x, 32, 64);
+// Value of x held by lane l ^ 32 (the other lane of this query column).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second.  Swapping x against 0 twice moves each half of x
+// to the other half and leaves 0 where the data did not come from, so the OR
+// of the two results is the partner value.  (A single swap of x with itself
+// would do, but the compiler treats the two results of swap(x, x) as equal.)
+__device__ __forceinline__ float partner32(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto lo = __builtin_amdgcn_permlane32_swap(u, 0u, false, false);  // lanes 0-31 of [1] <- x[32..63]
+    const auto hi = __builtin_amdgcn_permlane32_swap(0u, u, false, false);  // lanes 32-63 of [0] <- x[0..31]
+    return __builtin_bit_cast(float, lo[1] | hi[0]);
 }
+__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, partner32(x)); }
+__device__ __forceinline__ float pair_sum(float x) { return x + partner32(x); }
 
 // HBM -> LDS copy of one K or V tile (kBN rows of D bf16 starting at key kv0),
 // each wave moving kSegs / NW wave-wide 1 KiB segments.  Row r of the tile
-// lives at LDS byte r * kRowBytes with its chunks permuted by `swz`.
+// lives at LDS byte r * kRowBytes with its chunks permuted by the swizzle.
 template <int D, int NW, bool IS_V>
 __device__ __forceinline__ void load_tile(const bf16* __restrict__ base, size_t row_stride, int kv0, int n,
-                                          LDS_AS char* tile, int wave, int lane) {
+                                          LDS_AS char* __restrict__ tile, int wave, int lane) {
     using Ly = Layout<D>;
     static_assert(Ly::kSegs % NW == 0, "tile copy must split evenly over waves");
 #pragma unroll
@@ -104,12 +117,118 @@ __device__ __forceinline__ void load_tile(const bf16* __restrict__ base, size_t 
     }
 }
 
+// Running state of one wave: 32 query rows, online softmax in base 2.
+template <int D>
+struct WaveState {
+    static constexpr int KSTEPS = D / 16;
+    static constexpr int DBLK = D / 32;
+    bf16x8 qf[KSTEPS];  // Q fragment (B operand of S^T = K Q^T)
+    f32x16 oacc[DBLK];  // O^T accumulator: column = this lane's query
+    float m_run;        // reference max of raw scores (equal in lanes l, l^32)
+    float l_run;        // sum of the bf16 probabilities this lane contributed
+    int koff[KSTEPS];   // LDS byte offsets of the K operand per k step
+    int voff[DBLK];     // LDS byte offsets of the transposed V reads per O^T block
+};
+
+// Rescaling is deferred until a tile's max exceeds the reference max by this
+// many powers of two, so probabilities stay below 2^kRescaleLog2.
+constexpr float kRescaleLog2 = 8.f;
+
+// One key tile: issue the copies of the next tile, then S^T, softmax and O^T
+// update from the current tile.  The buffers are restrict-qualified so that
+// the compiler knows the copies into *_next never alias the reads of *_cur.
+template <int D, int NW>
+__device__ __forceinline__ void attend_tile(WaveState<D>& st, const LDS_AS char* __restrict__ kcur,
+                                            const LDS_AS char* __restrict__ vcur, LDS_AS char* __restrict__ knext,
+                                            LDS_AS char* __restrict__ vnext, bool load_next, const bf16* kbase,
+                                            const bf16* vbase, size_t row_stride, int kv_next, int n, int lim,
+                                            float c, int wave, int lane) {
+    using Ly = Layout<D>;
+    constexpr int KSTEPS = WaveState<D>::KSTEPS;
+    constexpr int DBLK = WaveState<D>::DBLK;
+    const int h = lane >> 5;
+    if (load_next) {
+        load_tile<D, NW, false>(kbase, row_stride, kv_next, n, knext, wave, lane);
+        load_tile<D, NW, true>(vbase, row_stride, kv_next, n, vnext, wave, lane);
+    }
+    // S^T block kb: rows = keys kb*32 .. +31, columns = this wave's queries
+    f32x16 s[kBN / 32];
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            const bf16x8 kf = *reinterpret_cast<const LDS_AS bf16x8*>(kcur + kb * 32 * Ly::kRowBytes + st.koff[t]);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[t], s[kb], 0, 0, 0);
+        }
+    }
+    if (lim < kBN) {  // keys past the window end (last tile only)
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                s[kb][r] = key < lim ? s[kb][r] : -INFINITY;
+            }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+    mx = pair_max(mx);
+    const bool grow = (mx - st.m_run) * c > kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : st.m_run;
+        const float alpha = __builtin_amdgcn_exp2f((st.m_run - m_new) * c);
+        st.m_run = m_new;
+        st.l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+    }
+    const float mc = st.m_run * c;
+    // P^T as bf16 B operands, one per 16-key step; the row sum adds the
+    // rounded bf16 values, i.e. exactly the weights the P V product uses
+    bf16x8 pb[kBN / 16];
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+    float rs = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < kBN / 16; ++jj) {
+        const int kb = jj >> 1, r0 = 8 * (jj & 1);
+        f32x8 x;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i], c, -mc));
+        pb[jj] = __builtin_convertvector(x, bf16x8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2 pr = {pb[jj][2 * i], pb[jj][2 * i + 1]};
+            rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+        }
+    }
+    st.l_run += rs;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int jj = 0; jj < kBN / 16; ++jj) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            const LDS_AS char* a0 = vcur + st.voff[db] + (16 * jj) * Ly::kRowBytes;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * Ly::kRowBytes));
+            const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[jj],
+                                                                  st.oacc[db], 0, 0, 0);
+        }
+    }
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     using Ly = Layout<D>;
     constexpr int BM = 32 * NW;
-    constexpr int KSTEPS = D / 16;   // 16-wide k steps of Q K^T
-    constexpr int DBLK = D / 32;     // 32-row blocks of O^T
+    constexpr int KSTEPS = WaveState<D>::KSTEPS;
+    constexpr int DBLK = WaveState<D>::DBLK;
     __shared__ __attribute__((aligned(1024))) char smem[4 * Ly::kTileBytes];
     LDS_AS char* lds = (LDS_AS char*)smem;
     LDS_AS char* kbuf[2] = {lds, lds + Ly::kTileBytes};
@@ -145,133 +264,50 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     load_tile<D, NW, false>(kbase, row_stride, 0, n, kbuf[0], wave, lane);
     load_tile<D, NW, true>(vbase, row_stride, 0, n, vbuf[0], wave, lane);
 
-    // ---- Q fragment: B operand of S^T = K Q^T, kept in registers ----------
+    WaveState<D> st;
     const int qrow = q0 + wave * 32 + (lane & 31);
-    const int qrow_c = qrow < n ? qrow : n - 1;
-    bf16x8 qf[KSTEPS];
     {
+        const int qrow_c = qrow < n ? qrow : n - 1;
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(p.q + base_off + (size_t)qrow_c * row_stride);
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) qf[t] = qp[2 * t + h];
+        for (int t = 0; t < KSTEPS; ++t) st.qf[t] = qp[2 * t + h];
     }
-
-    // ---- per-lane LDS offsets ---------------------------------------------
     // K (A operand of S^T): lane reads row (lane % 32) of a 32-key block,
     // logical chunk 2t + h.
-    int koff[KSTEPS];
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
         const int r = lane & 31;
-        koff[t] = r * Ly::kRowBytes + Ly::k_chunk(r, 2 * t + h) * 16;
+        st.koff[t] = r * Ly::kRowBytes + Ly::k_chunk(r, 2 * t + h) * 16;
     }
     // V (A operand of O^T, transposed read): address-supplying lane s of
     // 16-lane group g points at row 4*(g/2) + e, column 16*(g%2) + 4*c of a
     // 16-key x 32-column block (e = (s/4)%4, c = s%4); the transposed read
     // hands lane l the four rows 4*(l/32)+{0..3} of column l % 32.
-    int voff[DBLK];
     {
         const int g = lane >> 4, e = (lane >> 2) & 3, c = lane & 3;
         const int r = 4 * (g >> 1) + e;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
             const int lc = db * 4 + 2 * (g & 1) + (c >> 1);
-            voff[db] = r * Ly::kRowBytes + Ly::v_chunk(r, lc) * 16 + (c & 1) * 8;
+            st.voff[db] = r * Ly::kRowBytes + Ly::v_chunk(r, lc) * 16 + (c & 1) * 8;
         }
     }
-
-    float m_run = -INFINITY;  // running max of raw scores of this lane's query
-    float l_run = 0.f;        // running sum over the keys this lane holds
-    f32x16 oacc[DBLK];
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
+    for (int db = 0; db < DBLK; ++db) st.oacc[db] = f32x16{};
 
     for (int j = 0; j < nkv; ++j) {
         const int cur = j & 1;
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile j have landed
         __syncthreads();                      // ... and every wave's; tile j-1 buffers are free
-        if (j + 1 < nkv) {
-            load_tile<D, NW, false>(kbase, row_stride, (j + 1) * kBN, n, kbuf[cur ^ 1], wave, lane);
-            load_tile<D, NW, true>(vbase, row_stride, (j + 1) * kBN, n, vbuf[cur ^ 1], wave, lane);
-        }
-        const LDS_AS char* kt = kbuf[cur];
-        const LDS_AS char* vt = vbuf[cur];
-
-        // S^T block kb: rows = keys kb*32 .. +31, columns = this wave's queries
-        f32x16 s[kBN / 32];
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb) {
-            s[kb] = f32x16{};
-#pragma unroll
-            for (int t = 0; t < KSTEPS; ++t) {
-                const bf16x8 kf = *reinterpret_cast<const LDS_AS bf16x8*>(kt + kb * 32 * Ly::kRowBytes + koff[t]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
-            }
-        }
-        // keys past the window end (last tile only)
-        if ((j + 1) * kBN > n) {
-            const int lim = n - j * kBN;
-#pragma unroll
-            for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (key >= lim) s[kb][r] = -INFINITY;
-                }
-        }
-        // online softmax (base 2, scale folded into one FMA)
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, wave_xor32(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * p.scale_log2);
-        const float mc = m_new * p.scale_log2;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.scale_log2, -mc));
-                s[kb][r] = e;
-                rs += e;
-            }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-        // P^T as bf16 B operands, one per 16-key step
-        bf16x8 pb[kBN / 16];
-#pragma unroll
-        for (int jj = 0; jj < kBN / 16; ++jj) {
-            const int kb = jj >> 1, r0 = 8 * (jj & 1);
-            f32x8 x;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = s[kb][r0 + i];
-            pb[jj] = __builtin_convertvector(x, bf16x8);
-        }
-        // O^T += V^T P^T
-#pragma unroll
-        for (int jj = 0; jj < kBN / 16; ++jj) {
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
-                const LDS_AS char* a0 = vt + voff[db] + (16 * jj) * Ly::kRowBytes;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * Ly::kRowBytes));
-                typedef short i16x8 __attribute__((ext_vector_type(8)));
-                const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[jj], oacc[db],
-                                                                   0, 0, 0);
-            }
-        }
+        const int lim = n - j * kBN;
+        attend_tile<D, NW>(st, kbuf[cur], vbuf[cur], kbuf[cur ^ 1], vbuf[cur ^ 1], j + 1 < nkv, kbase, vbase,
+                           row_stride, (j + 1) * kBN, n, lim, p.scale_log2, wave, lane);
     }
 
     // ---- epilogue ------------------------------------------------------------
-    const float l_tot = l_run + wave_xor32(l_run);
+    const float l_tot = pair_sum(st.l_run);
     const float inv = 1.f / l_tot;
     if (qrow < n) {
         bf16* orow = p.o + base_off + (size_t)qrow * row_stride;
@@ -281,12 +317,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
             for (int a = 0; a < 4; ++a) {
                 f32x4 x;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = oacc[db][4 * a + i] * inv;
+                for (int i = 0; i < 4; ++i) x[i] = st.oacc[db][4 * a + i] * inv;
                 const bf16x4 y = __builtin_convertvector(x, bf16x4);
                 *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * a + 4 * h) = y;
             }
         if (p.lse && h == 0) {
-            p.lse[((size_t)b * p.heads + head) * p.L + start + qrow] = m_run * p.scale + logf(l_tot);
+            p.lse[((size_t)b * p.heads + head) * p.L + start + qrow] = st.m_run * p.scale + logf(l_tot);
         }
     }
 }
