@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--workload", default="video_21x45x80")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only time a plain device-to-device copy of one workload tensor (the reference kernel of "
+                         "known size for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -178,6 +181,21 @@ def main():
     w = BY_NAME[args.workload]
     dev = "cuda"
     wa.load_library()
+    if args.copy_calibration:
+        x = torch.empty((w.batch, w.L, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev).fill_(1.0)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            y.copy_(x)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        nbytes = x.numel() * 2
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms_per_copy": round(ms, 4),
+                          "gbps": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
+        return
     log(f"[bench] {w.name}: grid {w.T}x{w.H}x{w.W} B={w.batch} heads={w.heads} D={w.head_dim} "
         f"entry={w.entry} schedule={','.join(w.schedule)}")
     st = Step(w, wa, torch, dev)

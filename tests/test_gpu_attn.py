@@ -14,8 +14,8 @@ import window_attention_amd as wa
 from oracle import attention as oatt
 from oracle import permute as operm
 from oracle import plan as oplan
-from tests.gpu_helpers import LSE_ABS, MAX_ABS, MEAN_ABS, assert_close_full, check_window_head, method_of, say, \
-    to_f64
+from tests.gpu_helpers import MAX_ABS, MEAN_ABS, assert_close_full, check_window_head, lse_bound, lse_bound_windows, \
+    method_of, say, to_f64
 from window_attention_amd.inputs import normal, qkv
 from window_attention_amd.workloads import WORKLOADS
 
@@ -39,8 +39,9 @@ def test_ragged_segments_full_compare(D, lengths):
     L, B, Hh = int(cu[-1]), 2, 3
     q, k, v = (normal((B, L, Hh, D), 500 + t, device=DEV) for t in range(3))
     o, lse = wa.attn_fwd(q, k, v, torch.as_tensor(cu, device=DEV), max(lengths), return_lse=True)
-    ref_o, ref_lse = oatt.window_attention(to_f64(q), to_f64(k), to_f64(v), cu)
-    assert_close_full(o, lse, ref_o, ref_lse)
+    qh, kh = to_f64(q), to_f64(k)
+    ref_o, ref_lse = oatt.window_attention(qh, kh, to_f64(v), cu)
+    assert_close_full(o, lse, ref_o, ref_lse, lse_bound_windows(qh, kh, cu))
 
 
 def test_rows_outside_windows_untouched_and_empty_plan():
@@ -50,8 +51,10 @@ def test_rows_outside_windows_untouched_and_empty_plan():
     out = torch.full_like(q, 7.0)
     lse = wa.attn_fwd(q, k, v, cu, 40, out=out, return_lse=True)[1]
     assert torch.all(out[:, 70:] == 7.0)
-    ref_o, ref_lse = oatt.window_attention(to_f64(q), to_f64(k), to_f64(v), [0, 40, 70])
-    assert_close_full(out[:, :70], lse[:, :, :70], ref_o[:, :70], ref_lse[:, :, :70])
+    qh, kh = to_f64(q), to_f64(k)
+    ref_o, ref_lse = oatt.window_attention(qh, kh, to_f64(v), [0, 40, 70])
+    tol = lse_bound_windows(qh, kh, [0, 40, 70])
+    assert_close_full(out[:, :70], lse[:, :, :70], ref_o[:, :70], ref_lse[:, :, :70], tol[:, :, :70])
     # no windows at all: nothing is written
     out2 = torch.full_like(q, 3.0)
     wa.attn_fwd(q, k, v, torch.zeros(1, dtype=torch.int32, device=DEV), 0, out=out2)
@@ -73,7 +76,8 @@ def test_closed_forms_on_device():
         a, e = cu[i], cu[i + 1]
         mean = vh[:, a:e].mean(axis=1, keepdims=True)
         assert np.max(np.abs(to_f64(o[:, a:e]) - mean)) <= MAX_ABS
-        assert np.max(np.abs(lse[:, :, a:e].cpu().numpy() - math.log(n))) <= LSE_ABS
+        # q = 0: every score is 0 exactly, so only the normaliser's rounding is left
+        assert np.max(np.abs(lse[:, :, a:e].cpu().numpy() - math.log(n))) <= 2.0 ** -9 + 5e-4
 
 
 @pytest.mark.parametrize("method", [0, 1])
@@ -90,8 +94,11 @@ def test_tiny_clip_both_layouts(method):
     o = wa.scatter(ow, p.perm)
     op = oplan.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, method)
     win = np.repeat(np.arange(op.num_windows), np.diff(op.cu_seqlens))[np.asarray(op.inv)]
-    ref_o, ref_lse = oatt.masked_full_attention(to_f64(q), to_f64(k), to_f64(v), win)
-    assert_close_full(o, lse[:, :, p.inv.long()], ref_o, ref_lse)
+    qh, kh = to_f64(q), to_f64(k)
+    ref_o, ref_lse = oatt.masked_full_attention(qh, kh, to_f64(v), win)
+    # per-row LSE bound computed in window order, then taken to canonical order
+    tol = lse_bound_windows(operm.gather(qh, op.perm), operm.gather(kh, op.perm), op.cu_seqlens)[:, :, op.inv]
+    assert_close_full(o, lse[:, :, p.inv.long()], ref_o, ref_lse, tol)
 
 
 def test_clip_720p_full_compare():
@@ -104,10 +111,10 @@ def test_clip_720p_full_compare():
     ow, lse = wa.attn_fwd(qw, kw, vw, p.cu_seqlens, p.max_seqlen, return_lse=True)
     o = wa.scatter(ow, p.perm)
     op = oplan.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, 0)
-    ref_w, ref_lse = oatt.window_attention(operm.gather(to_f64(q), op.perm), operm.gather(to_f64(k), op.perm),
-                                           operm.gather(to_f64(v), op.perm), op.cu_seqlens)
+    qw_h, kw_h = operm.gather(to_f64(q), op.perm), operm.gather(to_f64(k), op.perm)
+    ref_w, ref_lse = oatt.window_attention(qw_h, kw_h, operm.gather(to_f64(v), op.perm), op.cu_seqlens)
     assert_close_full(o, None, operm.scatter(ref_w, op.perm), None)
-    assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ABS
+    assert np.all(np.abs(lse.double().cpu().numpy() - ref_lse) <= lse_bound_windows(qw_h, kw_h, op.cu_seqlens))
 
 
 def _sample_windows(cu, rng, extra=2):
@@ -157,10 +164,10 @@ def test_full_size_workloads_sampled(wi):
             for i in _sample_windows(cu, rng):
                 for h in sorted({0, w.heads - 1, int(rng.integers(0, w.heads))}):
                     mx, mean, lerr, n = check_window_head(qw, kw, vw, o, lse, cu, b, i, h)
-                    assert mx <= MAX_ABS and mean <= MEAN_ABS and lerr <= LSE_ABS, (w.name, li, b, i, h, n, mx,
-                                                                                     mean, lerr)
+                    assert mx <= MAX_ABS and mean <= MEAN_ABS and lerr <= 1.0, (w.name, li, b, i, h, n, mx,
+                                                                                mean, lerr)
                     worst = tuple(max(a, c) for a, c in zip(worst, (mx, mean, lerr)))
-        say(f"{w.name} layer {li} ({lay}): worst max={worst[0]:.3e} mean={worst[1]:.3e} lse={worst[2]:.3e}")
+        say(f"{w.name} layer {li} ({lay}): worst max={worst[0]:.3e} mean={worst[1]:.3e} lse/bound={worst[2]:.3f}")
 
 
 def test_batch_invariance_hd_grid():

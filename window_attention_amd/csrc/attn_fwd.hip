@@ -51,6 +51,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBN = 64;          // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct AttnParams {
     const bf16* q;
@@ -96,38 +97,81 @@ __device__ __forceinline__ float partner32(float x) {
 __device__ __forceinline__ float pair_max(float x) { return fmaxf(x, partner32(x)); }
 __device__ __forceinline__ float pair_sum(float x) { return x + partner32(x); }
 
-// HBM -> LDS copy of one K or V tile (kBN rows of D bf16 starting at key kv0),
-// each wave moving kSegs / NW wave-wide 1 KiB segments.  Row r of the tile
-// lives at LDS byte r * kRowBytes with its chunks permuted by the swizzle.
+// HBM -> LDS copy of one K or V tile (kBN rows of D bf16 starting at key
+// kv0), each wave moving kSegs / NW wave-wide 1 KiB segments.  Row r of the
+// tile lives at LDS byte r * kRowBytes with its 16-byte chunks permuted by the
+// swizzle.  Segment i of this lane copies tile row seg_row(i) (lane / kCPR
+// within the segment), logical chunk seg_chunk(i).
 template <int D, int NW, bool IS_V>
-__device__ __forceinline__ void load_tile(const bf16* __restrict__ base, size_t row_stride, int kv0, int n,
-                                          LDS_AS char* __restrict__ tile, int wave, int lane) {
+struct TileCopy {
     using Ly = Layout<D>;
+    static constexpr int kPerWave = Ly::kSegs / NW;
     static_assert(Ly::kSegs % NW == 0, "tile copy must split evenly over waves");
-#pragma unroll
-    for (int i = 0; i < Ly::kSegs / NW; ++i) {
-        const int seg = wave * (Ly::kSegs / NW) + i;
-        const int row = seg * Ly::kRowsPerSeg + lane / Ly::kCPR;
-        const int pc = lane % Ly::kCPR;
-        const int lc = IS_V ? Ly::v_chunk(row, pc) : Ly::k_chunk(row, pc);  // xor swizzles are involutions
-        int key = kv0 + row;
-        key = key < n ? key : n - 1;
-        const bf16* g = base + (size_t)key * row_stride + lc * 8;
-        __builtin_amdgcn_global_load_lds((const void*)g, (LDS_AS void*)(tile + seg * 1024), 16, 0, 0);
+    // chunk_xor relies on: rows per segment a power of two (so the segment
+    // part and the lane part of a row index occupy disjoint bits) and every
+    // wave's first row a multiple of the chunk count.
+    static_assert((Ly::kRowsPerSeg & (Ly::kRowsPerSeg - 1)) == 0, "rows per segment must be a power of two");
+    static_assert((kPerWave * Ly::kRowsPerSeg) % Ly::kCPR == 0, "wave segments must start at a swizzle period");
+    __device__ static int seg_row(int wave, int lane, int i) {
+        return (wave * kPerWave + i) * Ly::kRowsPerSeg + lane / Ly::kCPR;
     }
-}
+    __device__ static int seg_chunk(int wave, int lane, int i) {
+        const int row = seg_row(wave, lane, i), pc = lane % Ly::kCPR;
+        return IS_V ? Ly::v_chunk(row, pc) : Ly::k_chunk(row, pc);  // xor swizzles are involutions
+    }
+    // Byte offset of this lane's source for segment i, relative to tile row
+    // 0.  The segments of one lane are kRowsPerSeg rows apart (a uniform
+    // offset); their logical chunks differ by an XOR that only touches bits
+    // of the chunk index: for K (swizzle r % kCPR, rows 4i + g for D = 128)
+    // chunk(i) = chunk(0) ^ (kRowsPerSeg * i % kCPR), for V (swizzle of
+    // r % 4, the same for every segment) chunk(i) = chunk(0).
+    __device__ static uint32_t src_off0(size_t row_stride, int wave, int lane) {
+        return (uint32_t)(((size_t)seg_row(wave, lane, 0) * row_stride + seg_chunk(wave, lane, 0) * 8) * 2);
+    }
+    __device__ static constexpr uint32_t chunk_xor(int i) {
+        return IS_V ? 0u : (uint32_t)(((i * Ly::kRowsPerSeg) & (Ly::kCPR - 1)) * 16);
+    }
+    // every row of the tile inside the window: uniform base + fixed offsets
+    __device__ static void full(const char* __restrict__ base, uint32_t off0, size_t row_stride,
+                                LDS_AS char* __restrict__ tile, int wave) {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            const char* b = base + (size_t)i * Ly::kRowsPerSeg * row_stride * 2;
+            __builtin_amdgcn_global_load_lds((const void*)(b + (off0 ^ chunk_xor(i))),
+                                             (LDS_AS void*)(tile + (wave * kPerWave + i) * 1024), 16, 0, 0);
+        }
+    }
+    // last tile: rows past the window end re-read its last row
+    __device__ static void clamped(const bf16* __restrict__ base, size_t row_stride, int kv0, int n,
+                                   LDS_AS char* __restrict__ tile, int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            int key = kv0 + seg_row(wave, lane, i);
+            key = key < n ? key : n - 1;
+            const bf16* g = base + (size_t)key * row_stride + seg_chunk(wave, lane, i) * 8;
+            __builtin_amdgcn_global_load_lds((const void*)g, (LDS_AS void*)(tile + (wave * kPerWave + i) * 1024), 16,
+                                             0, 0);
+        }
+    }
+};
 
 // Running state of one wave: 32 query rows, online softmax in base 2.
-template <int D>
+// Scores are kept relative to a reference max m_ref (in log2 units of the
+// scaled scores); the score MFMA chain starts from the splat -m_ref, so the
+// probabilities are plain exp2 of the accumulator.
+template <int D, int NW>
 struct WaveState {
     static constexpr int KSTEPS = D / 16;
     static constexpr int DBLK = D / 32;
-    bf16x8 qf[KSTEPS];  // Q fragment (B operand of S^T = K Q^T)
+    bf16x8 qf[KSTEPS];  // Q * scale * log2(e), B operand of S^T = K Q^T
     f32x16 oacc[DBLK];  // O^T accumulator: column = this lane's query
-    float m_run;        // reference max of raw scores (equal in lanes l, l^32)
+    f32x16 neg_ref;     // splat(-m_ref)
+    float m_ref;        // reference max (equal in lanes l and l ^ 32)
     float l_run;        // sum of the bf16 probabilities this lane contributed
-    int koff[KSTEPS];   // LDS byte offsets of the K operand per k step
+    int koff0;          // LDS byte offset of the K operand at k step 0 (step t: ^ 32 t)
     int voff[DBLK];     // LDS byte offsets of the transposed V reads per O^T block
+    uint32_t kcopy;     // source offset of this lane's first K tile segment
+    uint32_t vcopy;     // source offset of this lane's first V tile segment
 };
 
 // Rescaling is deferred until a tile's max exceeds the reference max by this
@@ -138,57 +182,74 @@ constexpr float kRescaleLog2 = 8.f;
 // update from the current tile.  The buffers are restrict-qualified so that
 // the compiler knows the copies into *_next never alias the reads of *_cur.
 template <int D, int NW>
-__device__ __forceinline__ void attend_tile(WaveState<D>& st, const LDS_AS char* __restrict__ kcur,
+__device__ __forceinline__ void attend_tile(WaveState<D, NW>& st, const LDS_AS char* __restrict__ kcur,
                                             const LDS_AS char* __restrict__ vcur, LDS_AS char* __restrict__ knext,
-                                            LDS_AS char* __restrict__ vnext, bool load_next, const bf16* kbase,
-                                            const bf16* vbase, size_t row_stride, int kv_next, int n, int lim,
-                                            float c, int wave, int lane) {
+                                            LDS_AS char* __restrict__ vnext, const bf16* kbase, const bf16* vbase,
+                                            size_t row_stride, int kv, int n, bool first, int wave, int lane) {
     using Ly = Layout<D>;
-    constexpr int KSTEPS = WaveState<D>::KSTEPS;
-    constexpr int DBLK = WaveState<D>::DBLK;
+    constexpr int KSTEPS = WaveState<D, NW>::KSTEPS;
+    constexpr int DBLK = WaveState<D, NW>::DBLK;
     const int h = lane >> 5;
-    if (load_next) {
-        load_tile<D, NW, false>(kbase, row_stride, kv_next, n, knext, wave, lane);
-        load_tile<D, NW, true>(vbase, row_stride, kv_next, n, vnext, wave, lane);
+    const int kv_next = kv + kBN;
+    // Keep the per-lane bases opaque to loop-invariant code motion: the
+    // offsets derived from them by XOR / add with constants are cheaper to
+    // recompute each tile than to hold in registers across the loop.
+    asm volatile("" : "+v"(st.koff0), "+v"(st.kcopy), "+v"(st.vcopy));
+    if (kv_next + kBN <= n) {
+        const size_t adv = (size_t)kv_next * row_stride * 2;
+        TileCopy<D, NW, false>::full(reinterpret_cast<const char*>(kbase) + adv, st.kcopy, row_stride, knext, wave);
+        TileCopy<D, NW, true>::full(reinterpret_cast<const char*>(vbase) + adv, st.vcopy, row_stride, vnext, wave);
+    } else if (kv_next < n) {
+        TileCopy<D, NW, false>::clamped(kbase, row_stride, kv_next, n, knext, wave, lane);
+        TileCopy<D, NW, true>::clamped(vbase, row_stride, kv_next, n, vnext, wave, lane);
     }
-    // S^T block kb: rows = keys kb*32 .. +31, columns = this wave's queries
+    // S'^T block kb = K Q'^T - m_ref: rows = keys kb*32 .. +31, columns = queries
     f32x16 s[kBN / 32];
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
-        s[kb] = f32x16{};
+        s[kb] = st.neg_ref;
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) {
-            const bf16x8 kf = *reinterpret_cast<const LDS_AS bf16x8*>(kcur + kb * 32 * Ly::kRowBytes + st.koff[t]);
+            const bf16x8 kf =
+                *reinterpret_cast<const LDS_AS bf16x8*>(kcur + kb * 32 * Ly::kRowBytes + (st.koff0 ^ (32 * t)));
             s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[t], s[kb], 0, 0, 0);
         }
     }
+    const int lim = n - kv;
     if (lim < kBN) {  // keys past the window end (last tile only)
+        // key of register r in block kb is kb*32 + 8*(r/4) + 4h + r%4:
+        // compare the constant part against the limit less the lane part
+        const int lim_h = lim - 4 * h;
 #pragma unroll
         for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                s[kb][r] = key < lim ? s[kb][r] : -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+                s[kb][r] = kb * 32 + 8 * (r >> 2) + (r & 3) < lim_h ? s[kb][r] : -INFINITY;
     }
-    float mx = -INFINITY;
+    float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-    mx = pair_max(mx);
-    const bool grow = (mx - st.m_run) * c > kRescaleLog2;
+    for (int r = 0; r < 16; r += 2) {
+        mx0 = fmaxf(fmaxf(mx0, s[0][r]), s[0][r + 1]);
+        mx1 = fmaxf(fmaxf(mx1, s[1][r]), s[1][r + 1]);
+    }
+    const float mx = pair_max(fmaxf(mx0, mx1));
+    const bool grow = first || mx > kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mx : st.m_run;
-        const float alpha = __builtin_amdgcn_exp2f((st.m_run - m_new) * c);
-        st.m_run = m_new;
+        const float delta = grow ? mx : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        st.m_ref += delta;
         st.l_run *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.neg_ref[r] = -st.m_ref;
     }
-    const float mc = st.m_run * c;
     // P^T as bf16 B operands, one per 16-key step; the row sum adds the
     // rounded bf16 values, i.e. exactly the weights the P V product uses
     bf16x8 pb[kBN / 16];
@@ -199,7 +260,7 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& st, const LDS_AS char*
         const int kb = jj >> 1, r0 = 8 * (jj & 1);
         f32x8 x;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i], c, -mc));
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(s[kb][r0 + i]);
         pb[jj] = __builtin_convertvector(x, bf16x8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -224,15 +285,18 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& st, const LDS_AS char*
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     using Ly = Layout<D>;
+    using St = WaveState<D, NW>;
     constexpr int BM = 32 * NW;
-    constexpr int KSTEPS = WaveState<D>::KSTEPS;
-    constexpr int DBLK = WaveState<D>::DBLK;
+    constexpr int KSTEPS = St::KSTEPS;
+    constexpr int DBLK = St::DBLK;
     __shared__ __attribute__((aligned(1024))) char smem[4 * Ly::kTileBytes];
     LDS_AS char* lds = (LDS_AS char*)smem;
-    LDS_AS char* kbuf[2] = {lds, lds + Ly::kTileBytes};
-    LDS_AS char* vbuf[2] = {lds + 2 * Ly::kTileBytes, lds + 3 * Ly::kTileBytes};
+    LDS_AS char* const k0 = lds;
+    LDS_AS char* const k1 = lds + Ly::kTileBytes;
+    LDS_AS char* const v0 = lds + 2 * Ly::kTileBytes;
+    LDS_AS char* const v1 = lds + 3 * Ly::kTileBytes;
 
     // ---- work item: XCD-aware decomposition of blockIdx ------------------
     const int bid = blockIdx.x;
@@ -260,24 +324,38 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     const bf16* kbase = p.k + base_off;
     const bf16* vbase = p.v + base_off;
 
+    St st;
+    st.kcopy = TileCopy<D, NW, false>::src_off0(row_stride, wave, lane);
+    st.vcopy = TileCopy<D, NW, true>::src_off0(row_stride, wave, lane);
     const int nkv = (n + kBN - 1) / kBN;
-    load_tile<D, NW, false>(kbase, row_stride, 0, n, kbuf[0], wave, lane);
-    load_tile<D, NW, true>(vbase, row_stride, 0, n, vbuf[0], wave, lane);
+    if (kBN <= n) {
+        TileCopy<D, NW, false>::full(reinterpret_cast<const char*>(kbase), st.kcopy, row_stride, k0, wave);
+        TileCopy<D, NW, true>::full(reinterpret_cast<const char*>(vbase), st.vcopy, row_stride, v0, wave);
+    } else {
+        TileCopy<D, NW, false>::clamped(kbase, row_stride, 0, n, k0, wave, lane);
+        TileCopy<D, NW, true>::clamped(vbase, row_stride, 0, n, v0, wave, lane);
+    }
 
-    WaveState<D> st;
     const int qrow = q0 + wave * 32 + (lane & 31);
     {
         const int qrow_c = qrow < n ? qrow : n - 1;
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(p.q + base_off + (size_t)qrow_c * row_stride);
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) st.qf[t] = qp[2 * t + h];
-    }
-    // K (A operand of S^T): lane reads row (lane % 32) of a 32-key block,
-    // logical chunk 2t + h.
+        for (int t = 0; t < KSTEPS; ++t) {
+            const bf16x8 x = qp[2 * t + h];
+            f32x8 y;
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
+            for (int i = 0; i < 8; ++i) y[i] = (float)x[i] * p.scale_log2;
+            st.qf[t] = __builtin_convertvector(y, bf16x8);
+        }
+    }
+    // K (A operand of S^T): lane reads row r = lane % 32 of a 32-key block,
+    // logical chunk 2t + h, stored at chunk (2t + h) ^ (r % kCPR).  The t
+    // part only flips chunk bits above bit 0, so the offset of step t is the
+    // step-0 offset XOR 32 t.
+    {
         const int r = lane & 31;
-        st.koff[t] = r * Ly::kRowBytes + Ly::k_chunk(r, 2 * t + h) * 16;
+        st.koff0 = r * Ly::kRowBytes + Ly::k_chunk(r, h) * 16;
     }
     // V (A operand of O^T, transposed read): address-supplying lane s of
     // 16-lane group g points at row 4*(g/2) + e, column 16*(g%2) + 4*c of a
@@ -292,18 +370,26 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
             st.voff[db] = r * Ly::kRowBytes + Ly::v_chunk(r, lc) * 16 + (c & 1) * 8;
         }
     }
-    st.m_run = -INFINITY;
+    st.m_ref = 0.f;
     st.l_run = 0.f;
+    st.neg_ref = f32x16{};
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) st.oacc[db] = f32x16{};
 
-    for (int j = 0; j < nkv; ++j) {
-        const int cur = j & 1;
+    // key tiles in pairs, so that the LDS buffers of each are compile-time
+    int j = 0;
+    for (; j + 1 < nkv; j += 2) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile j have landed
-        __syncthreads();                      // ... and every wave's; tile j-1 buffers are free
-        const int lim = n - j * kBN;
-        attend_tile<D, NW>(st, kbuf[cur], vbuf[cur], kbuf[cur ^ 1], vbuf[cur ^ 1], j + 1 < nkv, kbase, vbase,
-                           row_stride, (j + 1) * kBN, n, lim, p.scale_log2, wave, lane);
+        __syncthreads();                      // ... and every wave's; the other buffers are free
+        attend_tile<D, NW>(st, k0, v0, k1, v1, kbase, vbase, row_stride, j * kBN, n, j == 0, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        attend_tile<D, NW>(st, k1, v1, k0, v0, kbase, vbase, row_stride, (j + 1) * kBN, n, false, wave, lane);
+    }
+    if (j < nkv) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        attend_tile<D, NW>(st, k0, v0, k1, v1, kbase, vbase, row_stride, j * kBN, n, j == 0, wave, lane);
     }
 
     // ---- epilogue ------------------------------------------------------------
@@ -322,7 +408,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
                 *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * a + 4 * h) = y;
             }
         if (p.lse && h == 0) {
-            p.lse[((size_t)b * p.heads + head) * p.L + start + qrow] = st.m_run * p.scale + logf(l_tot);
+            // sum_k exp(scale * s_k) = 2^m_ref * l_tot
+            p.lse[((size_t)b * p.heads + head) * p.L + start + qrow] = st.m_ref * kLn2 + logf(l_tot);
         }
     }
 }
