@@ -7,8 +7,8 @@
 // softmax over key tiles, so the n x n score matrix never leaves registers.
 //
 // Mapping to CDNA4
-//   * One workgroup = NW waves = a tile of 32*NW query rows of one (batch,
-//     window, head).  Each wave owns 32 query rows.
+//   * One workgroup = NW waves = a tile of 32*QB*NW query rows of one
+//     (batch, window, head).  Each wave owns QB blocks of 32 query rows.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator layout a lane holds
 //     16 keys of ONE query column (lane % 32), so the softmax row max and row
@@ -20,11 +20,17 @@
 //     read with ds_read_b64_tr_b16, which returns four rows of one column per
 //     lane, so V needs no transpose pass.  The O^T accumulator column is again
 //     the lane's own query, so the online-softmax rescale is per lane.
+//   * Every K or V fragment read from LDS feeds QB MFMAs (one per query
+//     block), so LDS read traffic per flop falls as 1 / QB.
 //   * K and V tiles (64 keys) are copied HBM -> LDS with
 //     global_load_lds_dwordx4 (no VGPR staging), double buffered.  Rows are
 //     stored with an XOR swizzle of their 16-byte chunks so that the K reads
 //     (32 rows, same chunk) and the transposed V reads (4 rows x 4 columns per
 //     16 lanes) are spread over the LDS banks.
+//   * The key loop is software pipelined: while the MFMAs of tile j+1's
+//     scores run, the VALU packs tile j's probabilities; while the MFMAs of
+//     tile j's P V product run, the VALU does tile j+1's row max and exp2.
+//     Scheduling-group hints lay the two instruction streams out interleaved.
 //   * Grid: blockIdx % 8 selects the XCD; all query tiles of one (batch,
 //     window, head) go to the same XCD, consecutively, so they share its L2
 //     while they stream the same K/V tiles.
@@ -40,18 +46,25 @@ namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kBN = 64;          // keys per tile
+constexpr int kBN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+
+// Rescaling is deferred until a tile's max exceeds the reference max by this
+// many powers of two, so probabilities stay below 2^kRescaleLog2.
+constexpr float kRescaleLog2 = 8.f;
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedVALU = 0x002;
+constexpr int kSchedMFMA = 0x008;
+constexpr int kSchedDSRead = 0x100;
 
 struct AttnParams {
     const bf16* q;
@@ -63,20 +76,20 @@ struct AttnParams {
     int32_t num_windows;
     int32_t L;
     int32_t heads;
-    int32_t qtiles;      // query tiles per (batch, window, head) in the grid
-    int32_t pairs;       // batch * num_windows * heads
-    float scale;         // softmax scale
-    float scale_log2;    // softmax scale * log2(e)
+    int32_t qtiles;    // query tiles per (batch, window, head) in the grid
+    int32_t pairs;     // batch * num_windows * heads
+    float scale;       // softmax scale
+    float scale_log2;  // softmax scale * log2(e)
 };
 
 template <int D>
 struct Layout {
-    static constexpr int kCPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int kCPR = D / 8;  // 16-byte chunks per row
     static constexpr int kRowBytes = D * 2;
     static constexpr int kTileBytes = kBN * kRowBytes;
-    static constexpr int kSegs = kTileBytes / 1024;    // wave-wide 1 KiB copies per tile
+    static constexpr int kSegs = kTileBytes / 1024;  // wave-wide 1 KiB copies per tile
     static constexpr int kRowsPerSeg = 1024 / kRowBytes;
-    static constexpr int kVSwz = kCPR >= 16 ? 4 : 2;   // V chunk swizzle stride
+    static constexpr int kVSwz = kCPR >= 16 ? 4 : 2;  // V chunk swizzle stride
     // physical 16-byte chunk of logical chunk c in row r
     __device__ static int k_chunk(int r, int c) { return c ^ (r & (kCPR - 1)); }
     __device__ static int v_chunk(int r, int c) { return c ^ (kVSwz * (r & 3)); }
@@ -107,11 +120,12 @@ struct TileCopy {
     using Ly = Layout<D>;
     static constexpr int kPerWave = Ly::kSegs / NW;
     static_assert(Ly::kSegs % NW == 0, "tile copy must split evenly over waves");
-    // chunk_xor relies on: rows per segment a power of two (so the segment
-    // part and the lane part of a row index occupy disjoint bits) and every
-    // wave's first row a multiple of the chunk count.
+    // chunk_xor relies on the row index wave * kPerWave * kRowsPerSeg +
+    // i * kRowsPerSeg + lane / kCPR having its three parts in disjoint bits,
+    // so that adding them is XOR-ing them: both strides powers of two.
     static_assert((Ly::kRowsPerSeg & (Ly::kRowsPerSeg - 1)) == 0, "rows per segment must be a power of two");
-    static_assert((kPerWave * Ly::kRowsPerSeg) % Ly::kCPR == 0, "wave segments must start at a swizzle period");
+    static_assert(((kPerWave * Ly::kRowsPerSeg) & (kPerWave * Ly::kRowsPerSeg - 1)) == 0,
+                  "rows per wave must be a power of two");
     __device__ static int seg_row(int wave, int lane, int i) {
         return (wave * kPerWave + i) * Ly::kRowsPerSeg + lane / Ly::kCPR;
     }
@@ -122,8 +136,9 @@ struct TileCopy {
     // Byte offset of this lane's source for segment i, relative to tile row
     // 0.  The segments of one lane are kRowsPerSeg rows apart (a uniform
     // offset); their logical chunks differ by an XOR that only touches bits
-    // of the chunk index: for K (swizzle r % kCPR, rows 4i + g for D = 128)
-    // chunk(i) = chunk(0) ^ (kRowsPerSeg * i % kCPR), for V (swizzle of
+    // of the chunk index: for K (swizzle r % kCPR) the row's segment part
+    // i * kRowsPerSeg shares no bit with the rest of the row index, so
+    // chunk(i) = chunk(0) ^ (i * kRowsPerSeg % kCPR); for V (swizzle of
     // r % 4, the same for every segment) chunk(i) = chunk(0).
     __device__ static uint32_t src_off0(size_t row_stride, int wave, int lane) {
         return (uint32_t)(((size_t)seg_row(wave, lane, 0) * row_stride + seg_chunk(wave, lane, 0) * 8) * 2);
@@ -155,68 +170,77 @@ struct TileCopy {
     }
 };
 
-// Running state of one wave: 32 query rows, online softmax in base 2.
-// Scores are kept relative to a reference max m_ref (in log2 units of the
-// scaled scores); the score MFMA chain starts from the splat -m_ref, so the
-// probabilities are plain exp2 of the accumulator.
-template <int D, int NW>
+// Copies of one K or V tile into LDS: the whole tile inside the window from
+// a uniform base, else (last tile) with rows clamped to the window.
+template <int D, int NW, bool IS_V>
+__device__ __forceinline__ void copy_tile(uint32_t off0, const bf16* base, size_t row_stride, int kv, int n,
+                                          LDS_AS char* __restrict__ dst, int wave, int lane) {
+    using TC = TileCopy<D, NW, IS_V>;
+    if (kv + kBN <= n) {
+        TC::full(reinterpret_cast<const char*>(base) + (size_t)kv * row_stride * 2, off0, row_stride, dst, wave);
+    } else {
+        TC::clamped(base, row_stride, kv, n, dst, wave, lane);
+    }
+}
+
+// Running state of one wave: QB blocks of 32 query rows, online softmax in
+// base 2.  Probabilities are exp2(c * s - c * m_ref) with c = softmax_scale *
+// log2(e) and m_ref a reference max of the raw scores s.
+template <int D, int QB>
 struct WaveState {
     static constexpr int KSTEPS = D / 16;
     static constexpr int DBLK = D / 32;
-    bf16x8 qf[KSTEPS];  // Q * scale * log2(e), B operand of S^T = K Q^T
-    f32x16 oacc[DBLK];  // O^T accumulator: column = this lane's query
-    f32x16 neg_ref;     // splat(-m_ref)
-    float m_ref;        // reference max (equal in lanes l and l ^ 32)
-    float l_run;        // sum of the bf16 probabilities this lane contributed
-    int koff0;          // LDS byte offset of the K operand at k step 0 (step t: ^ 32 t)
-    int voff[DBLK];     // LDS byte offsets of the transposed V reads per O^T block
-    uint32_t kcopy;     // source offset of this lane's first K tile segment
-    uint32_t vcopy;     // source offset of this lane's first V tile segment
+    bf16x8 qf[QB][KSTEPS];  // Q fragments, B operands of S^T = K Q^T
+    f32x16 oacc[QB][DBLK];  // O^T accumulators: column = this lane's query
+    float m_ref[QB];        // reference max of the raw scores (equal in lanes l and l ^ 32)
+    float mc[QB];           // c * m_ref
+    float l_run[QB];        // sum of the bf16 probabilities this lane contributed
+    float alpha[QB];        // O rescale factor owed since the reference last moved
+    bool pending;           // wave-uniform: alpha must be applied before the next P V
+    int koff0;              // LDS byte offset of the K operand at k step 0 (step t: ^ 32 t)
+    int voff[DBLK];         // LDS byte offsets of the transposed V reads per O^T block
+    uint32_t kcopy;         // source offset of this lane's first K tile segment
+    uint32_t vcopy;         // source offset of this lane's first V tile segment
 };
 
-// Rescaling is deferred until a tile's max exceeds the reference max by this
-// many powers of two, so probabilities stay below 2^kRescaleLog2.
-constexpr float kRescaleLog2 = 8.f;
-
-// One key tile: issue the copies of the next tile, then S^T, softmax and O^T
-// update from the current tile.  The buffers are restrict-qualified so that
-// the compiler knows the copies into *_next never alias the reads of *_cur.
-template <int D, int NW>
-__device__ __forceinline__ void attend_tile(WaveState<D, NW>& st, const LDS_AS char* __restrict__ kcur,
-                                            const LDS_AS char* __restrict__ vcur, LDS_AS char* __restrict__ knext,
-                                            LDS_AS char* __restrict__ vnext, const bf16* kbase, const bf16* vbase,
-                                            size_t row_stride, int kv, int n, bool first, int wave, int lane) {
+// K fragment (A operand of S^T) number i of a key tile: fragments alternate
+// between the two 32-key blocks (independent accumulator chains), so
+// fragment i is block i % 2, k step i / 2.
+template <int D, int QB>
+__device__ __forceinline__ bf16x8 k_fragment(const WaveState<D, QB>& st, const LDS_AS char* __restrict__ kt, int i) {
     using Ly = Layout<D>;
-    constexpr int KSTEPS = WaveState<D, NW>::KSTEPS;
-    constexpr int DBLK = WaveState<D, NW>::DBLK;
-    const int h = lane >> 5;
-    const int kv_next = kv + kBN;
-    // Keep the per-lane bases opaque to loop-invariant code motion: the
-    // offsets derived from them by XOR / add with constants are cheaper to
-    // recompute each tile than to hold in registers across the loop.
-    asm volatile("" : "+v"(st.koff0), "+v"(st.kcopy), "+v"(st.vcopy));
-    if (kv_next + kBN <= n) {
-        const size_t adv = (size_t)kv_next * row_stride * 2;
-        TileCopy<D, NW, false>::full(reinterpret_cast<const char*>(kbase) + adv, st.kcopy, row_stride, knext, wave);
-        TileCopy<D, NW, true>::full(reinterpret_cast<const char*>(vbase) + adv, st.vcopy, row_stride, vnext, wave);
-    } else if (kv_next < n) {
-        TileCopy<D, NW, false>::clamped(kbase, row_stride, kv_next, n, knext, wave, lane);
-        TileCopy<D, NW, true>::clamped(vbase, row_stride, kv_next, n, vnext, wave, lane);
-    }
-    // S'^T block kb = K Q'^T - m_ref: rows = keys kb*32 .. +31, columns = queries
-    f32x16 s[kBN / 32];
+    return *reinterpret_cast<const LDS_AS bf16x8*>(kt + (i & 1) * 32 * Ly::kRowBytes + (st.koff0 ^ (32 * (i >> 1))));
+}
+
+// S^T = K Q^T for one key tile: s[qb][kb] holds keys kb*32 .. +31 (rows)
+// against query block qb (columns).  K fragments are read two fragments ahead
+// of their use; each feeds QB MFMAs.
+template <int D, int QB>
+__device__ __forceinline__ void tile_scores(const WaveState<D, QB>& st, const LDS_AS char* __restrict__ kt,
+                                            f32x16 (&s)[QB][kBN / 32]) {
+    constexpr int N = (kBN / 32) * WaveState<D, QB>::KSTEPS;
+    static_assert(kBN / 32 == 2, "fragment order alternates two score blocks");
+    bf16x8 kf[2];
+    kf[0] = k_fragment(st, kt, 0);
+    kf[1] = k_fragment(st, kt, 1);
 #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) {
-        s[kb] = st.neg_ref;
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-            const bf16x8 kf =
-                *reinterpret_cast<const LDS_AS bf16x8*>(kcur + kb * 32 * Ly::kRowBytes + (st.koff0 ^ (32 * t)));
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[t], s[kb], 0, 0, 0);
-        }
+    for (int qb = 0; qb < QB; ++qb) {
+        s[qb][0] = f32x16{};
+        s[qb][1] = f32x16{};
     }
-    const int lim = n - kv;
-    if (lim < kBN) {  // keys past the window end (last tile only)
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const bf16x8 a = kf[i & 1];
+        if (i + 2 < N) kf[i & 1] = k_fragment(st, kt, i + 2);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            s[qb][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[qb][i >> 1], s[qb][i & 1], 0, 0, 0);
+    }
+}
+
+// Keys past the window end (the last tile only) get score -inf.
+__device__ __forceinline__ void mask_tail(f32x16 (&s)[kBN / 32], int lim, int h) {
+    if (lim < kBN) {
         // key of register r in block kb is kb*32 + 8*(r/4) + 4h + r%4:
         // compare the constant part against the limit less the lane part
         const int lim_h = lim - 4 * h;
@@ -226,69 +250,241 @@ __device__ __forceinline__ void attend_tile(WaveState<D, NW>& st, const LDS_AS c
             for (int r = 0; r < 16; ++r)
                 s[kb][r] = kb * 32 + 8 * (r >> 2) + (r & 3) < lim_h ? s[kb][r] : -INFINITY;
     }
+}
+
+// Row max of one query block's score tile (equal in lanes l and l ^ 32).
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[kBN / 32]) {
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
         mx0 = fmaxf(fmaxf(mx0, s[0][r]), s[0][r + 1]);
         mx1 = fmaxf(fmaxf(mx1, s[1][r]), s[1][r + 1]);
     }
-    const float mx = pair_max(fmaxf(mx0, mx1));
-    const bool grow = first || mx > kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float delta = grow ? mx : 0.f;
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-        st.m_ref += delta;
-        st.l_run *= alpha;
+    return pair_max(fmaxf(mx0, mx1));
+}
+
+// Move the reference max of growing lanes of query block qb to the tile max
+// and rebase the running sum.  Returns the factor O must be multiplied by once
+// every earlier P V product is in it (1 for lanes whose reference did not
+// move).
+template <int D, int QB>
+__device__ __forceinline__ float move_reference(WaveState<D, QB>& st, int qb, float mx, bool grow, float c) {
+    const float m_new = grow ? mx : st.m_ref[qb];
+    const float alpha = __builtin_amdgcn_exp2f((st.m_ref[qb] - m_new) * c);
+    st.m_ref[qb] = m_new;
+    st.mc[qb] = m_new * c;
+    st.l_run[qb] *= alpha;
+    return alpha;
+}
+
+// exp2 of one query block's scores against its reference, in place (fp32
+// probabilities, at most 2^kRescaleLog2).
+__device__ __forceinline__ void tile_exp(f32x16 (&s)[kBN / 32], float c, float mc) {
 #pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
+    for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.neg_ref[r] = -st.m_ref;
-    }
-    // P^T as bf16 B operands, one per 16-key step; the row sum adds the
-    // rounded bf16 values, i.e. exactly the weights the P V product uses
-    bf16x8 pb[kBN / 16];
+        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mc));
+}
+
+// bf16 probabilities (B operands of the P V product, one per 16 keys) and
+// their row sums; a sum adds the rounded bf16 values, i.e. exactly the
+// weights the P V product uses.
+template <int D, int QB>
+__device__ __forceinline__ void tile_pack(WaveState<D, QB>& st, const f32x16 (&pf)[QB][kBN / 32],
+                                          bf16x8 (&pb)[QB][kBN / 16]) {
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-    float rs = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < kBN / 16; ++jj) {
-        const int kb = jj >> 1, r0 = 8 * (jj & 1);
-        f32x8 x;
+    for (int qb = 0; qb < QB; ++qb) {
+        float rs = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(s[kb][r0 + i]);
-        pb[jj] = __builtin_convertvector(x, bf16x8);
+        for (int jj = 0; jj < kBN / 16; ++jj) {
+            const int kb = jj >> 1, r0 = 8 * (jj & 1);
+            f32x8 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bf16x2 pr = {pb[jj][2 * i], pb[jj][2 * i + 1]};
-            rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+            for (int i = 0; i < 8; ++i) x[i] = pf[qb][kb][r0 + i];
+            pb[qb][jj] = __builtin_convertvector(x, bf16x8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bf16x2 pr = {pb[qb][jj][2 * i], pb[qb][jj][2 * i + 1]};
+                rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+            }
         }
-    }
-    st.l_run += rs;
-    // O^T += V^T P^T
-#pragma unroll
-    for (int jj = 0; jj < kBN / 16; ++jj) {
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-            const LDS_AS char* a0 = vcur + st.voff[db] + (16 * jj) * Ly::kRowBytes;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * Ly::kRowBytes));
-            const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[jj],
-                                                                  st.oacc[db], 0, 0, 0);
-        }
+        st.l_run[qb] += rs;
     }
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
+// V^T fragment (A operand of O^T block `voff`) for 16-key step jj.
+template <int D>
+__device__ __forceinline__ bf16x8 v_fragment(const LDS_AS char* __restrict__ vt, int voff, int jj) {
     using Ly = Layout<D>;
-    using St = WaveState<D, NW>;
-    constexpr int BM = 32 * NW;
+    const LDS_AS char* a0 = vt + voff + (16 * jj) * Ly::kRowBytes;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * Ly::kRowBytes));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// O^T += V^T P^T for V fragments i0 .. i1-1 of one key tile (fragment i =
+// 16-key step i / DBLK, O^T block i % DBLK; each feeds QB MFMAs).  vf is a
+// ring of fragments read kAhead ahead of their use: on entry it holds those
+// of i0 .. i0 + kAhead - 1, on exit those of i1 .. i1 + kAhead - 1.
+constexpr int kAhead = 2;
+
+template <int D, int QB, int i0, int i1>
+__device__ __forceinline__ void tile_pv(WaveState<D, QB>& st, const LDS_AS char* __restrict__ vt,
+                                        const bf16x8 (&pb)[QB][kBN / 16], bf16x8 (&vf)[kAhead]) {
+    constexpr int DBLK = WaveState<D, QB>::DBLK;
+    constexpr int N = DBLK * (kBN / 16);
+#pragma unroll
+    for (int i = i0; i < i1; ++i) {
+        const bf16x8 a = vf[i % kAhead];
+        if (i + kAhead < N) vf[i % kAhead] = v_fragment<D>(vt, st.voff[(i + kAhead) % DBLK], (i + kAhead) / DBLK);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            st.oacc[qb][i % DBLK] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][i / DBLK], st.oacc[qb][i % DBLK], 0, 0, 0);
+    }
+}
+
+template <int D, int QB>
+__device__ __forceinline__ void tile_pv_begin(const WaveState<D, QB>& st, const LDS_AS char* __restrict__ vt,
+                                              bf16x8 (&vf)[kAhead]) {
+    constexpr int DBLK = WaveState<D, QB>::DBLK;
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) vf[i] = v_fragment<D>(vt, st.voff[i % DBLK], i / DBLK);
+}
+
+// Ask the scheduler to lay out the current straight-line region as
+// `ds_first` LDS reads, then `groups` x {`mfma` MFMAs, `ds` LDS reads, `valu`
+// VALU}.  With operands read ahead (the order the code issues them in), every
+// MFMA finds its operands already in flight.
+template <int groups, int ds_first, int mfma, int ds, int valu>
+__device__ __forceinline__ void interleave_mfma() {
+    if (ds_first) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, ds_first, 0);
+#pragma unroll
+    for (int i = 0; i < groups; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, mfma, 0);
+        if (ds) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, ds, 0);
+        if (valu) __builtin_amdgcn_sched_group_barrier(kSchedVALU, valu, 0);
+    }
+}
+
+// Deferred rescale of O by alpha (a move of the reference max, applied once
+// every P V product computed against the old reference is in O).
+template <int D, int QB>
+__device__ __forceinline__ void apply_pending_rescale(WaveState<D, QB>& st) {
+    if (st.pending) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int db = 0; db < WaveState<D, QB>::DBLK; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st.oacc[qb][db][r] *= st.alpha[qb];
+        st.pending = false;
+    }
+}
+
+// One pipelined step j (j + 1 < number of key tiles).  On entry pf holds the
+// fp32 probabilities of tile j (against the current references); on exit
+// those of tile j+1.  Work is split into two MFMA streams with independent
+// VALU work between their instructions:
+//   scores:  S(j+1) = K(j+1) Q^T          || bf16 P(j) and its row sums
+//   values:  O += V(j)^T P(j)^T            || row max, exp2 of S(j+1)
+// plus the copies of K(j+2) and V(j+1) into the buffers read in step j-1.
+template <int D, int NW, int QB>
+__device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)[QB][kBN / 32],
+                                              const LDS_AS char* __restrict__ k_next,
+                                              const LDS_AS char* __restrict__ v_cur, LDS_AS char* __restrict__ k_fill,
+                                              LDS_AS char* __restrict__ v_fill, const bf16* kbase, const bf16* vbase,
+                                              size_t row_stride, int j, int n, float c, int wave, int lane) {
+    constexpr int DBLK = WaveState<D, QB>::DBLK;
+    constexpr int KSTEPS = WaveState<D, QB>::KSTEPS;
+    // keep the per-lane bases opaque to loop-invariant code motion: offsets
+    // derived from them by XOR / add with constants are cheaper to recompute
+    // each step than to hold in registers across the loop
+    asm volatile("" : "+v"(st.koff0), "+v"(st.kcopy), "+v"(st.vcopy));
+    const int h = lane >> 5;
+    apply_pending_rescale(st);
+    if ((j + 2) * kBN < n) copy_tile<D, NW, false>(st.kcopy, kbase, row_stride, (j + 2) * kBN, n, k_fill, wave, lane);
+    if ((j + 1) * kBN < n) copy_tile<D, NW, true>(st.vcopy, vbase, row_stride, (j + 1) * kBN, n, v_fill, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    // scores stream
+    bf16x8 pb[QB][kBN / 16];
+    f32x16 s[QB][kBN / 32];
+    tile_scores(st, k_next, s);
+    tile_pack(st, pf, pb);
+    bf16x8 vf[kAhead];
+    tile_pv_begin(st, v_cur, vf);
+    // the bf16 probabilities and their sums are needed here, not only after
+    // the mask below
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+        asm volatile("" ::"v"(pb[qb][0]), "v"(pb[qb][1]), "v"(pb[qb][2]), "v"(pb[qb][3]), "v"(st.l_run[qb]));
+    interleave_mfma<(kBN / 32) * KSTEPS, 2, QB, 1, 4 * QB>();
+    __builtin_amdgcn_sched_barrier(0);
+    const int lim = n - (j + 1) * kBN;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mask_tail(s[qb], lim, h);
+    __builtin_amdgcn_sched_barrier(0);
+    // values stream, part A: first 16 keys with the row maxes of S(j+1)
+    tile_pv<D, QB, 0, DBLK>(st, v_cur, pb, vf);
+    float mx[QB];
+    bool grow[QB];
+    bool any_grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        mx[qb] = tile_max(s[qb]);
+        grow[qb] = (mx[qb] - st.m_ref[qb]) * c > kRescaleLog2;
+        any_grow |= grow[qb];
+    }
+    const bool rescale = __builtin_amdgcn_ballot_w64(any_grow) != 0;
+    interleave_mfma<DBLK, 0, QB, 2, 6 * QB>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (rescale) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) st.alpha[qb] = move_reference(st, qb, mx[qb], grow[qb], c);
+        st.pending = true;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // values stream, part B: the remaining 48 keys with exp2 of S(j+1)
+    tile_pv<D, QB, DBLK, DBLK*(kBN / 16)>(st, v_cur, pb, vf);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) tile_exp(s[qb], c, st.mc[qb]);
+    // the probabilities are needed here, not only in the next step
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" ::"v"(s[qb][0]), "v"(s[qb][1]));
+    interleave_mfma<DBLK*(kBN / 16 - 1), 0, QB, 2, 6 * QB>();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb) pf[qb][kb] = s[qb][kb];
+}
+
+// P V product of the last tile, whose probabilities are in pf.
+template <int D, int QB>
+__device__ __forceinline__ void final_pv(WaveState<D, QB>& st, const f32x16 (&pf)[QB][kBN / 32],
+                                         const LDS_AS char* __restrict__ v_cur) {
+    constexpr int DBLK = WaveState<D, QB>::DBLK;
+    apply_pending_rescale(st);
+    bf16x8 pb[QB][kBN / 16];
+    tile_pack(st, pf, pb);
+    bf16x8 vf[kAhead];
+    tile_pv_begin(st, v_cur, vf);
+    tile_pv<D, QB, 0, DBLK*(kBN / 16)>(st, v_cur, pb, vf);
+}
+
+// Waves per SIMD the register budget is sized for: one query block per wave
+// fits two waves per SIMD, two blocks need the whole register file of one.
+template <int QB>
+constexpr int waves_per_simd() {
+    return QB == 1 ? 2 : 1;
+}
+
+template <int D, int NW, int QB>
+__global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel(AttnParams p) {
+    using Ly = Layout<D>;
+    using St = WaveState<D, QB>;
+    constexpr int BM = 32 * QB * NW;
     constexpr int KSTEPS = St::KSTEPS;
     constexpr int DBLK = St::DBLK;
     __shared__ __attribute__((aligned(1024))) char smem[4 * Ly::kTileBytes];
@@ -323,31 +519,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const size_t base_off = ((size_t)b * p.L + start) * row_stride + (size_t)head * D;
     const bf16* kbase = p.k + base_off;
     const bf16* vbase = p.v + base_off;
+    const float c = p.scale_log2;
 
     St st;
     st.kcopy = TileCopy<D, NW, false>::src_off0(row_stride, wave, lane);
     st.vcopy = TileCopy<D, NW, true>::src_off0(row_stride, wave, lane);
     const int nkv = (n + kBN - 1) / kBN;
-    if (kBN <= n) {
-        TileCopy<D, NW, false>::full(reinterpret_cast<const char*>(kbase), st.kcopy, row_stride, k0, wave);
-        TileCopy<D, NW, true>::full(reinterpret_cast<const char*>(vbase), st.vcopy, row_stride, v0, wave);
-    } else {
-        TileCopy<D, NW, false>::clamped(kbase, row_stride, 0, n, k0, wave, lane);
-        TileCopy<D, NW, true>::clamped(vbase, row_stride, 0, n, v0, wave, lane);
-    }
+    copy_tile<D, NW, false>(st.kcopy, kbase, row_stride, 0, n, k0, wave, lane);
+    copy_tile<D, NW, true>(st.vcopy, vbase, row_stride, 0, n, v0, wave, lane);
 
-    const int qrow = q0 + wave * 32 + (lane & 31);
-    {
-        const int qrow_c = qrow < n ? qrow : n - 1;
-        const bf16x8* qp = reinterpret_cast<const bf16x8*>(p.q + base_off + (size_t)qrow_c * row_stride);
+    // query row of this lane in block qb: q0 + (wave * QB + qb) * 32 + lane % 32
+    const int qrow0 = q0 + wave * 32 * QB + (lane & 31);
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-            const bf16x8 x = qp[2 * t + h];
-            f32x8 y;
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qr = qrow0 + qb * 32;
+        const int qr_c = qr < n ? qr : n - 1;
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(p.q + base_off + (size_t)qr_c * row_stride);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] = (float)x[i] * p.scale_log2;
-            st.qf[t] = __builtin_convertvector(y, bf16x8);
-        }
+        for (int t = 0; t < KSTEPS; ++t) st.qf[qb][t] = qp[2 * t + h];
     }
     // K (A operand of S^T): lane reads row r = lane % 32 of a 32-key block,
     // logical chunk 2t + h, stored at chunk (2t + h) ^ (r % kCPR).  The t
@@ -362,70 +551,108 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     // 16-key x 32-column block (e = (s/4)%4, c = s%4); the transposed read
     // hands lane l the four rows 4*(l/32)+{0..3} of column l % 32.
     {
-        const int g = lane >> 4, e = (lane >> 2) & 3, c = lane & 3;
+        const int g = lane >> 4, e = (lane >> 2) & 3, cc = lane & 3;
         const int r = 4 * (g >> 1) + e;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-            const int lc = db * 4 + 2 * (g & 1) + (c >> 1);
-            st.voff[db] = r * Ly::kRowBytes + Ly::v_chunk(r, lc) * 16 + (c & 1) * 8;
+            const int lc = db * 4 + 2 * (g & 1) + (cc >> 1);
+            st.voff[db] = r * Ly::kRowBytes + Ly::v_chunk(r, lc) * 16 + (cc & 1) * 8;
         }
     }
-    st.m_ref = 0.f;
-    st.l_run = 0.f;
-    st.neg_ref = f32x16{};
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) st.oacc[db] = f32x16{};
-
-    // key tiles in pairs, so that the LDS buffers of each are compile-time
-    int j = 0;
-    for (; j + 1 < nkv; j += 2) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile j have landed
-        __syncthreads();                      // ... and every wave's; the other buffers are free
-        attend_tile<D, NW>(st, k0, v0, k1, v1, kbase, vbase, row_stride, j * kBN, n, j == 0, wave, lane);
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        attend_tile<D, NW>(st, k1, v1, k0, v0, kbase, vbase, row_stride, (j + 1) * kBN, n, false, wave, lane);
+    for (int qb = 0; qb < QB; ++qb) {
+        st.m_ref[qb] = 0.f;
+        st.mc[qb] = 0.f;
+        st.l_run[qb] = 0.f;
+        st.alpha[qb] = 1.f;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) st.oacc[qb][db] = f32x16{};
     }
-    if (j < nkv) {
+    st.pending = false;
+
+    // ---- prologue: tile 0 scores and probabilities ---------------------------
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile 0 have landed
+    __syncthreads();                      // ... and every wave's
+    if (kBN < n) copy_tile<D, NW, false>(st.kcopy, kbase, row_stride, kBN, n, k1, wave, lane);
+    f32x16 pf[QB][kBN / 32];
+    tile_scores(st, k0, pf);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        mask_tail(pf[qb], n, h);
+        move_reference(st, qb, tile_max(pf[qb]), true, c);  // first reference: the tile max (O is still zero)
+        tile_exp(pf[qb], c, st.mc[qb]);
+    }
+
+    // ---- pipelined key loop, steps in pairs so that LDS buffers are static ----
+    // step j reads K(j+1) from k[(j+1)%2] and V(j) from v[j%2]; it refills
+    // k[j%2] with K(j+2) and v[(j+1)%2] with V(j+1).  The last tile's P V runs
+    // after the loop.
+    int j = 0;
+    for (; j + 2 < nkv; j += 2) {
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        attend_tile<D, NW>(st, k0, v0, k1, v1, kbase, vbase, row_stride, j * kBN, n, j == 0, wave, lane);
+        pipeline_step<D, NW, QB>(st, pf, k1, v0, k0, v1, kbase, vbase, row_stride, j, n, c, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        pipeline_step<D, NW, QB>(st, pf, k0, v1, k1, v0, kbase, vbase, row_stride, j + 1, n, c, wave, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (j + 1 < nkv) {  // one more full step (tiles j, j+1), then the P V of tile j+1
+        pipeline_step<D, NW, QB>(st, pf, k1, v0, k0, v1, kbase, vbase, row_stride, j, n, c, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        final_pv(st, pf, v1);
+    } else {  // the P V of tile j
+        final_pv(st, pf, v0);
     }
 
     // ---- epilogue ------------------------------------------------------------
-    const float l_tot = pair_sum(st.l_run);
-    const float inv = 1.f / l_tot;
-    if (qrow < n) {
-        bf16* orow = p.o + base_off + (size_t)qrow * row_stride;
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qr = qrow0 + qb * 32;
+        const float l_tot = pair_sum(st.l_run[qb]);
+        const float inv = 1.f / l_tot;
+        if (qr < n) {
+            bf16* orow = p.o + base_off + (size_t)qr * row_stride;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                f32x4 x;
+            for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = st.oacc[db][4 * a + i] * inv;
-                const bf16x4 y = __builtin_convertvector(x, bf16x4);
-                *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * a + 4 * h) = y;
+                for (int a = 0; a < 4; ++a) {
+                    f32x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = st.oacc[qb][db][4 * a + i] * inv;
+                    const bf16x4 y = __builtin_convertvector(x, bf16x4);
+                    *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * a + 4 * h) = y;
+                }
+            if (p.lse && h == 0) {
+                // sum_k exp(scale * s_k) = exp(scale * m_ref) * l_tot
+                p.lse[((size_t)b * p.heads + head) * p.L + start + qr] = st.m_ref[qb] * p.scale + logf(l_tot);
             }
-        if (p.lse && h == 0) {
-            // sum_k exp(scale * s_k) = 2^m_ref * l_tot
-            p.lse[((size_t)b * p.heads + head) * p.L + start + qrow] = st.m_ref * kLn2 + logf(l_tot);
         }
     }
 }
 
-template <int D, int NW>
+template <int D, int NW, int QB>
 int launch_attn(const AttnParams& prm, int32_t max_seqlen, hipStream_t stream) {
-    constexpr int BM = 32 * NW;
+    constexpr int BM = 32 * QB * NW;
     AttnParams p = prm;
     p.qtiles = (max_seqlen + BM - 1) / BM;
     if (p.qtiles == 0 || p.pairs == 0) return WIN_OK;
     const int64_t groups = ((int64_t)p.pairs + 7) / 8;
     const int64_t blocks = groups * 8 * p.qtiles;
     if (blocks >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
-    attn_fwd_kernel<D, NW><<<dim3((uint32_t)blocks), dim3(NW * 64), 0, stream>>>(p);
+    attn_fwd_kernel<D, NW, QB><<<dim3((uint32_t)blocks), dim3(NW * 64), 0, stream>>>(p);
     return launch_status();
 }
+
+// Launch configuration: (waves per workgroup, query blocks per wave).
+#ifndef WINATTN_NW
+#define WINATTN_NW 4
+#endif
+#ifndef WINATTN_QB
+#define WINATTN_QB 1
+#endif
 
 }  // namespace
 }  // namespace winattn
@@ -466,6 +693,6 @@ extern "C" int win_attn_fwd(const void* q, const void* k, const void* v, void* o
     p.scale = softmax_scale;
     p.scale_log2 = softmax_scale * kLog2e;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (head_dim == 128) return launch_attn<128, 4>(p, max_seqlen, s);
-    return launch_attn<64, 4>(p, max_seqlen, s);
+    if (head_dim == 128) return launch_attn<128, WINATTN_NW, WINATTN_QB>(p, max_seqlen, s);
+    return launch_attn<64, WINATTN_NW, WINATTN_QB>(p, max_seqlen, s);
 }
