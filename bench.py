@@ -23,6 +23,8 @@ import time
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
 def log(*a):
@@ -116,6 +118,27 @@ class Step:
                 self.attn_events.append((a, b))
         pl = self.plans[cur]
         perm_launch(lambda: wa.scatter(self.o, pl.perm, out=self.out))
+
+
+def measured_traffic(kernel_prefix, workload):
+    """HBM bytes per launch (read + write) recorded in profiles/hbm_traffic.txt
+    for a kernel, or None when there is no record for this workload or the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("#") or not line.strip():
+            continue
+        rec = dict(kv.split("=", 1) for kv in line.split())
+        if not rec["kernel"].startswith(kernel_prefix) or rec.get("workload") != workload:
+            continue
+        src = os.path.join(ROOT, rec["source"])
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sha256"]:
+            return None
+        return {"fetch_bytes": int(rec["fetch_bytes"]), "write_bytes": int(rec["write_bytes"]),
+                "total_bytes": int(rec["fetch_bytes"]) + int(rec["write_bytes"])}
+    return None
 
 
 def cpu_baseline(w, seconds):
@@ -234,6 +257,8 @@ def main():
     log(f"[bench] permutes: {len(perm_ms) // args.steps}/step, mean {sum(perm_ms) / len(perm_ms) * 1e3:.1f} us, "
         f"{perm_gbs:.0f} GB/s")
     value = attn_flops_step / (ms_step * 1e-3) / 1e12
+    attn_traffic = measured_traffic("attn_fwd_kernel", w.name)
+    perm_traffic = measured_traffic("permute_rows_kernel<transition>", w.name)
     res = {
         "metric": "window-attn useful TFLOP/s + permute GB/s, 21x45x80 grid bf16, 1 GPU",
         "value": round(value, 2),
@@ -253,13 +278,17 @@ def main():
         "attn_tflops": round(attn_tfs, 2),
         "permute_gbps": round(perm_gbs, 1),
         "roofline": {"bound": "mfma", "achieved": round(attn_tfs, 2), "peak": BF16_MFMA_PEAK_TFS,
-                     "unit": "TFLOP/s", "frac": round(attn_tfs / BF16_MFMA_PEAK_TFS, 4), "traffic": None,
-                     "kernel": "attn_fwd_kernel<128,4>",
+                     "unit": "TFLOP/s", "frac": round(attn_tfs / BF16_MFMA_PEAK_TFS, 4),
+                     "traffic": attn_traffic["total_bytes"] if attn_traffic else None,
+                     "traffic_detail": attn_traffic,
+                     "kernel": "attn_fwd_kernel",
                      "avg_launch_ms": round(attn_ms_step / nl, 4),
                      "flops_per_launch": attn_flops_step / nl},
         "roofline_permute": {"bound": "hbm", "achieved": round(perm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(perm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                             "kernel": "permute_rows_kernel",
+                             "frac": round(perm_gbs / HBM_PEAK_GBS, 4),
+                             "traffic": perm_traffic["total_bytes"] if perm_traffic else None,
+                             "traffic_detail": perm_traffic,
+                             "kernel": "permute_rows_kernel (gather, transition, scatter)",
                              "avg_launch_ms": round(sum(perm_ms) / len(perm_ms), 4),
                              "bytes_per_launch": perm_bytes_launch},
     }

@@ -19,6 +19,12 @@ Readings where the page is silent (each is listed in the design notes):
 
 Everything here is Python integers except the three double operations of the
 size formula, so results are exact and reproducible.
+
+Parity unpinned by the pages: the page prints no window table, so the first
+two readings above (the cut of an odd window, no shift on a covered axis) are
+fixed only by the hand-derived worked examples written under them and by the
+invariants the page states; every other part of the plan is pinned by those
+invariants, exact-scale grids and the windowing-arange twin.
 """
 from __future__ import annotations
 
