@@ -149,8 +149,9 @@ int win_transition(const void* src, void* dst, const int32_t* inv_src, const int
  * Arithmetic: bf16 inputs, fp32 MFMA accumulation and fp32 online softmax,
  * bf16 output rounded to nearest even.  Deterministic: no atomics, a fixed
  * reduction order per output row, independent of batch size and grid.
- * Errors: WIN_EINVAL, WIN_EUNSUPPORTED (head_dim, alignment), WIN_EOVERFLOW,
- * WIN_EDEVICE.
+ * Errors: WIN_EINVAL, WIN_EUNSUPPORTED (head_dim, alignment), WIN_EOVERFLOW
+ * (L >= 2^31, batch * num_windows * heads >= 2^31, or heads * head_dim >=
+ * 2^24, so that 64 rows span 2^31 bytes or more), WIN_EDEVICE.
  */
 int win_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                  int32_t num_windows, int32_t max_seqlen, int64_t L, int32_t batch, int32_t heads,

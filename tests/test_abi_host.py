@@ -146,3 +146,7 @@ def test_device_entry_points_validate_before_launch():
     assert lib.win_attn_fwd(A, B, C, O, None, I, -1, 8, 8, 1, 1, 128, f(0.1), None) == -1
     assert lib.win_attn_fwd(A, B, C, O, None, I, 1, 8, 1 << 31, 1, 1, 128, f(0.1), None) == -3
     assert lib.win_attn_fwd(A, B, C, O, None, I, 0, 0, 8, 1, 1, 128, f(0.1), None) == 0   # no windows
+    # 64 rows of heads * head_dim bf16 must span less than 2^31 bytes (32-bit tile offsets)
+    Q2, K2, V2, O2 = (ctypes.c_void_p(i << 40) for i in (1, 2, 3, 4))
+    assert lib.win_attn_fwd(Q2, K2, V2, O2, None, I, 1, 8, 8, 1, 1 << 17, 128, f(0.1), None) == -3
+    assert lib.win_attn_fwd(Q2, K2, V2, O2, None, I, 0, 8, 8, 1, (1 << 17) - 1, 128, f(0.1), None) == 0

@@ -23,19 +23,23 @@
 //   * Every K or V fragment read from LDS feeds QB MFMAs (one per query
 //     block), so LDS read traffic per flop falls as 1 / QB.
 //   * K and V tiles (64 keys) are copied HBM -> LDS with
-//     global_load_lds_dwordx4 (no VGPR staging), double buffered.  Rows are
+//     buffer_load_dwordx4 ... lds (no VGPR staging), double buffered.  Rows are
 //     stored with an XOR swizzle of their 16-byte chunks so that the K reads
 //     (32 rows, same chunk) and the transposed V reads (4 rows x 4 columns per
 //     16 lanes) are spread over the LDS banks.
 //   * The key loop is software pipelined: while the MFMAs of tile j+1's
 //     scores run, the VALU packs tile j's probabilities; while the MFMAs of
 //     tile j's P V product run, the VALU does tile j+1's row max and exp2.
-//     Scheduling-group hints lay the two instruction streams out interleaved.
+//     The loop is laid out by hand in slots of one MFMA each, with the LDS
+//     reads of an operand issued a few MFMAs before its use and scheduling
+//     fences between slots, so that an MFMA never waits for a read issued
+//     just before it.
 //   * Grid: blockIdx % 8 selects the XCD; all query tiles of one (batch,
 //     window, head) go to the same XCD, consecutively, so they share its L2
 //     while they stream the same K/V tiles.
-//   * Rows past the end of a window are clamped to its last row on load and
-//     masked to -inf as keys, so no access leaves the window's tensors.
+//   * Query rows past the end of a window are clamped to its last row; key
+//     and value rows past it fail the copies' buffer range check and are
+//     masked to -inf as keys, so no access leaves the window's rows.
 #include <cmath>
 
 #include "common.h"
@@ -50,6 +54,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -60,11 +65,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Rescaling is deferred until a tile's max exceeds the reference max by this
 // many powers of two, so probabilities stay below 2^kRescaleLog2.
 constexpr float kRescaleLog2 = 8.f;
-
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedVALU = 0x002;
-constexpr int kSchedMFMA = 0x008;
-constexpr int kSchedDSRead = 0x100;
 
 struct AttnParams {
     const bf16* q;
@@ -146,42 +146,54 @@ struct TileCopy {
     __device__ static constexpr uint32_t chunk_xor(int i) {
         return IS_V ? 0u : (uint32_t)(((i * Ly::kRowsPerSeg) & (Ly::kCPR - 1)) * 16);
     }
-    // every row of the tile inside the window: uniform base + fixed offsets
-    __device__ static void full(const char* __restrict__ base, uint32_t off0, size_t row_stride,
-                                LDS_AS char* __restrict__ tile, int wave) {
-#pragma unroll
-        for (int i = 0; i < kPerWave; ++i) {
-            const char* b = base + (size_t)i * Ly::kRowsPerSeg * row_stride * 2;
-            __builtin_amdgcn_global_load_lds((const void*)(b + (off0 ^ chunk_xor(i))),
-                                             (LDS_AS void*)(tile + (wave * kPerWave + i) * 1024), 16, 0, 0);
-        }
-    }
-    // last tile: rows past the window end re-read its last row
-    __device__ static void clamped(const bf16* __restrict__ base, size_t row_stride, int kv0, int n,
-                                   LDS_AS char* __restrict__ tile, int wave, int lane) {
-#pragma unroll
-        for (int i = 0; i < kPerWave; ++i) {
-            int key = kv0 + seg_row(wave, lane, i);
-            key = key < n ? key : n - 1;
-            const bf16* g = base + (size_t)key * row_stride + seg_chunk(wave, lane, i) * 8;
-            __builtin_amdgcn_global_load_lds((const void*)g, (LDS_AS void*)(tile + (wave * kPerWave + i) * 1024), 16,
-                                             0, 0);
-        }
+    // segment i of this wave: per-lane offsets fixed for the whole loop,
+    // segment i a uniform kRowsPerSeg rows further
+    __device__ static void segment(__amdgpu_buffer_rsrc_t src, uint32_t off0, uint32_t seg_bytes,
+                                   LDS_AS char* __restrict__ tile, int wave, int i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (LDS_AS void*)(tile + (wave * kPerWave + i) * 1024), 16,
+                                                 off0 ^ chunk_xor(i), i * seg_bytes, 0, 0);
     }
 };
 
-// Copies of one K or V tile into LDS: the whole tile inside the window from
-// a uniform base, else (last tile) with rows clamped to the window.
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+
+// One pending HBM -> LDS tile copy, issued segment by segment.  The source is
+// a buffer resource based at the tile's first row and sized to the tile's rows
+// inside the window: offsets stay 32-bit, and rows past the window end fail
+// the range check, so no other window's data reaches the LDS (the rows keep
+// what the buffer held before: this window's earlier keys, or zeros).  A tile
+// past the last one gets an empty range and loads nothing.  Buffer (not
+// global) LDS-DMA loads also keep the compiler's LDS wait counts exact while
+// copies are in flight.
 template <int D, int NW, bool IS_V>
-__device__ __forceinline__ void copy_tile(uint32_t off0, const bf16* base, size_t row_stride, int kv, int n,
-                                          LDS_AS char* __restrict__ dst, int wave, int lane) {
+struct TileJob {
     using TC = TileCopy<D, NW, IS_V>;
-    if (kv + kBN <= n) {
-        TC::full(reinterpret_cast<const char*>(base) + (size_t)kv * row_stride * 2, off0, row_stride, dst, wave);
-    } else {
-        TC::clamped(base, row_stride, kv, n, dst, wave, lane);
+    __amdgpu_buffer_rsrc_t src;
+    uint32_t off0;       // per-lane source offset of segment 0
+    uint32_t seg_bytes;  // source bytes between consecutive segments of a lane
+    LDS_AS char* tile;
+
+    __device__ TileJob(uint32_t off0_, const bf16* base, size_t row_stride, int kv, int n, LDS_AS char* tile_)
+        : off0(off0_), tile(tile_) {
+        const uint32_t row_bytes = (uint32_t)row_stride * 2;
+        int rows = n - kv;
+        rows = rows < 0 ? 0 : (rows > kBN ? kBN : rows);
+        seg_bytes = TC::Ly::kRowsPerSeg * row_bytes;
+        // every input is wave-uniform; saying so keeps the resource in SGPRs
+        // (the compiler would otherwise wrap each load in a readfirstlane loop)
+        const uint64_t a = reinterpret_cast<uint64_t>(base + (size_t)kv * row_stride);
+        const uint64_t a_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+        src = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(a_u), 0,
+                                                __builtin_amdgcn_readfirstlane(rows * (int)row_bytes), kBufferWord3);
     }
-}
+    __device__ void issue(int wave, int i) const { TC::segment(src, off0, seg_bytes, tile, wave, i); }
+    __device__ void issue_all(int wave) const {
+#pragma unroll
+        for (int i = 0; i < TC::kPerWave; ++i) issue(wave, i);
+    }
+};
 
 // Running state of one wave: QB blocks of 32 query rows, online softmax in
 // base 2.  Probabilities are exp2(c * s - c * m_ref) with c = softmax_scale *
@@ -212,30 +224,21 @@ __device__ __forceinline__ bf16x8 k_fragment(const WaveState<D, QB>& st, const L
     return *reinterpret_cast<const LDS_AS bf16x8*>(kt + (i & 1) * 32 * Ly::kRowBytes + (st.koff0 ^ (32 * (i >> 1))));
 }
 
-// S^T = K Q^T for one key tile: s[qb][kb] holds keys kb*32 .. +31 (rows)
-// against query block qb (columns).  K fragments are read two fragments ahead
-// of their use; each feeds QB MFMAs.
-template <int D, int QB>
-__device__ __forceinline__ void tile_scores(const WaveState<D, QB>& st, const LDS_AS char* __restrict__ kt,
-                                            f32x16 (&s)[QB][kBN / 32]) {
-    constexpr int N = (kBN / 32) * WaveState<D, QB>::KSTEPS;
-    static_assert(kBN / 32 == 2, "fragment order alternates two score blocks");
-    bf16x8 kf[2];
-    kf[0] = k_fragment(st, kt, 0);
-    kf[1] = k_fragment(st, kt, 1);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        s[qb][0] = f32x16{};
-        s[qb][1] = f32x16{};
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const bf16x8 a = kf[i & 1];
-        if (i + 2 < N) kf[i & 1] = k_fragment(st, kt, i + 2);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            s[qb][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[qb][i >> 1], s[qb][i & 1], 0, 0, 0);
-    }
+// Instruction slots.  The key loop is laid out by hand as a sequence of
+// slots, each one MFMA (per query block), the LDS reads of the operand a
+// few MFMAs later and a share of the independent VALU work, closed by a
+// scheduling fence so that nothing migrates between slots.  Operands are thus
+// in flight kKAhead (K) or kVAhead (V) MFMAs ahead of their use, and the
+// waits before an MFMA are for its own operand only.
+constexpr int kKAhead = 3;
+constexpr int kVAhead = 2;
+__device__ __forceinline__ void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
+// A value computed in a slot is pinned there: without a use at this point the
+// compiler would sink the arithmetic to its first real use, a later slot or
+// the next step, past the fences (they only order machine scheduling).
+template <typename T>
+__device__ __forceinline__ void pin(const T& x) {
+    asm volatile("" ::"v"(x));
 }
 
 // Keys past the window end (the last tile only) get score -inf.
@@ -287,30 +290,34 @@ __device__ __forceinline__ void tile_exp(f32x16 (&s)[kBN / 32], float c, float m
 }
 
 // bf16 probabilities (B operands of the P V product, one per 16 keys) and
-// their row sums; a sum adds the rounded bf16 values, i.e. exactly the
-// weights the P V product uses.
-template <int D, int QB>
-__device__ __forceinline__ void tile_pack(WaveState<D, QB>& st, const f32x16 (&pf)[QB][kBN / 32],
-                                          bf16x8 (&pb)[QB][kBN / 16]) {
+// their row sums, split into kBN / 4 pieces of one bf16 pair each: piece i
+// converts keys 2i, 2i+1 of fragment i / 4 and adds them to the row sum, so
+// a sum adds exactly the rounded weights the P V product uses.
+struct PackedP {
+    uint32_t w[kBN / 16][4];  // bf16 pairs of the B operand of 16-key step jj
+};
+
+template <int QB>
+__device__ __forceinline__ void pack_piece(const f32x16 (&pf)[QB][kBN / 32], PackedP (&pp)[QB], float (&rs)[QB],
+                                           int i) {
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+    const int jj = i >> 2, m = i & 3;
+    const int kb = jj >> 1, r = 8 * (jj & 1) + 2 * m;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        float rs = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < kBN / 16; ++jj) {
-            const int kb = jj >> 1, r0 = 8 * (jj & 1);
-            f32x8 x;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = pf[qb][kb][r0 + i];
-            pb[qb][jj] = __builtin_convertvector(x, bf16x8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bf16x2 pr = {pb[qb][jj][2 * i], pb[qb][jj][2 * i + 1]};
-                rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
-            }
-        }
-        st.l_run[qb] += rs;
+        const f32x2 x = {pf[qb][kb][r], pf[qb][kb][r + 1]};
+        const bf16x2 pr = __builtin_convertvector(x, bf16x2);
+        pp[qb].w[jj][m] = __builtin_bit_cast(uint32_t, pr);
+        rs[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs[qb], false);
+        pin(pp[qb].w[jj][m]);
+        pin(rs[qb]);
     }
+}
+
+__device__ __forceinline__ bf16x8 p_operand(const PackedP& pp, int jj) {
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v w = {pp.w[jj][0], pp.w[jj][1], pp.w[jj][2], pp.w[jj][3]};
+    return __builtin_bit_cast(bf16x8, w);
 }
 
 // V^T fragment (A operand of O^T block `voff`) for 16-key step jj.
@@ -321,51 +328,6 @@ __device__ __forceinline__ bf16x8 v_fragment(const LDS_AS char* __restrict__ vt,
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * Ly::kRowBytes));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// O^T += V^T P^T for V fragments i0 .. i1-1 of one key tile (fragment i =
-// 16-key step i / DBLK, O^T block i % DBLK; each feeds QB MFMAs).  vf is a
-// ring of fragments read kAhead ahead of their use: on entry it holds those
-// of i0 .. i0 + kAhead - 1, on exit those of i1 .. i1 + kAhead - 1.
-constexpr int kAhead = 2;
-
-template <int D, int QB, int i0, int i1>
-__device__ __forceinline__ void tile_pv(WaveState<D, QB>& st, const LDS_AS char* __restrict__ vt,
-                                        const bf16x8 (&pb)[QB][kBN / 16], bf16x8 (&vf)[kAhead]) {
-    constexpr int DBLK = WaveState<D, QB>::DBLK;
-    constexpr int N = DBLK * (kBN / 16);
-#pragma unroll
-    for (int i = i0; i < i1; ++i) {
-        const bf16x8 a = vf[i % kAhead];
-        if (i + kAhead < N) vf[i % kAhead] = v_fragment<D>(vt, st.voff[(i + kAhead) % DBLK], (i + kAhead) / DBLK);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            st.oacc[qb][i % DBLK] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][i / DBLK], st.oacc[qb][i % DBLK], 0, 0, 0);
-    }
-}
-
-template <int D, int QB>
-__device__ __forceinline__ void tile_pv_begin(const WaveState<D, QB>& st, const LDS_AS char* __restrict__ vt,
-                                              bf16x8 (&vf)[kAhead]) {
-    constexpr int DBLK = WaveState<D, QB>::DBLK;
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) vf[i] = v_fragment<D>(vt, st.voff[i % DBLK], i / DBLK);
-}
-
-// Ask the scheduler to lay out the current straight-line region as
-// `ds_first` LDS reads, then `groups` x {`mfma` MFMAs, `ds` LDS reads, `valu`
-// VALU}.  With operands read ahead (the order the code issues them in), every
-// MFMA finds its operands already in flight.
-template <int groups, int ds_first, int mfma, int ds, int valu>
-__device__ __forceinline__ void interleave_mfma() {
-    if (ds_first) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, ds_first, 0);
-#pragma unroll
-    for (int i = 0; i < groups; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, mfma, 0);
-        if (ds) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, ds, 0);
-        if (valu) __builtin_amdgcn_sched_group_barrier(kSchedVALU, valu, 0);
-    }
 }
 
 // Deferred rescale of O by alpha (a move of the reference max, applied once
@@ -383,12 +345,92 @@ __device__ __forceinline__ void apply_pending_rescale(WaveState<D, QB>& st) {
     }
 }
 
+// K fragment i of a key tile, kept in a per-step array indexed by fragment
+// (the compiler allocates the few that are live at once).
+template <int D, int QB>
+__device__ __forceinline__ void read_k(const WaveState<D, QB>& st, const LDS_AS char* __restrict__ kt,
+                                       bf16x8* kf, int i) {
+    kf[i] = k_fragment(st, kt, i);
+}
+
+// Score slots of one key tile: S^T = K Q^T, s[qb][kb] holding keys kb*32 ..
+// +31 against query block qb.  Fragments alternate between the two 32-key
+// blocks (independent accumulator chains).  Slot i issues MFMA i and the read
+// of K fragment i + kKAhead.  Inside a pipeline step (PACK) it also packs
+// its share of the previous tile's probabilities and issues one segment of the
+// step's tile copies, and past the last K fragment it reads the first V
+// fragments of the P V product that follows.
+template <int D, int NW, int QB, bool PACK>
+__device__ __forceinline__ void score_slots(WaveState<D, QB>& st, const LDS_AS char* __restrict__ kt,
+                                            const LDS_AS char* __restrict__ vt, f32x16 (&s)[QB][kBN / 32],
+                                            bf16x8 (&vf)[WaveState<D, QB>::DBLK * (kBN / 16)],
+                                            const f32x16 (&pf)[QB][kBN / 32], PackedP (&pp)[QB], float (&rs)[QB],
+                                            const TileJob<D, NW, false>& kjob, const TileJob<D, NW, true>& vjob,
+                                            int wave) {
+    constexpr int KSEG = TileCopy<D, NW, false>::kPerWave;
+    constexpr int VSEG = TileCopy<D, NW, true>::kPerWave;
+    constexpr int DBLK = WaveState<D, QB>::DBLK;
+    constexpr int NS = (kBN / 32) * WaveState<D, QB>::KSTEPS;
+    static_assert(kBN / 32 == 2, "fragment order alternates two score blocks");
+    constexpr int PPS = (kBN / 4) / NS;  // pack pieces per slot
+    static_assert(PPS * NS == kBN / 4, "pack pieces must split evenly over the score slots");
+    static_assert(KSEG + VSEG <= NS, "one tile-copy segment per score slot");
+    bf16x8 kf[NS];
+#pragma unroll
+    for (int i = 0; i < kKAhead; ++i) read_k(st, kt, kf, i);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        s[qb][0] = f32x16{};
+        s[qb][1] = f32x16{};
+    }
+    slot_fence();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            s[qb][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], st.qf[qb][i >> 1], s[qb][i & 1], 0, 0, 0);
+        const int nx = i + kKAhead;
+        if (nx < NS)
+            read_k(st, kt, kf, nx);
+        else if (PACK && nx - NS < kVAhead)
+            vf[nx - NS] = v_fragment<D>(vt, st.voff[(nx - NS) % DBLK], (nx - NS) / DBLK);
+        if constexpr (PACK) {
+#pragma unroll
+            for (int pc = 0; pc < PPS; ++pc) pack_piece<QB>(pf, pp, rs, i * PPS + pc);
+            // tile copies for the next step, one segment per slot so that the
+            // vector-memory queue never holds up the wave
+            if (i < KSEG)
+                kjob.issue(wave, i);
+            else if (i < KSEG + VSEG)
+                vjob.issue(wave, i - KSEG);
+        }
+        slot_fence();
+    }
+}
+
+// Value slot i of one key tile: O^T block i % DBLK += V^T P^T over 16-key
+// step i / DBLK, and the read of V fragment i + kVAhead.  vf[0 .. kVAhead-1]
+// are in flight on entry.
+template <int D, int QB>
+__device__ __forceinline__ void value_slot(WaveState<D, QB>& st, const LDS_AS char* __restrict__ vt,
+                                           const PackedP (&pp)[QB], bf16x8 (&vf)[WaveState<D, QB>::DBLK * (kBN / 16)],
+                                           int i) {
+    constexpr int DBLK = WaveState<D, QB>::DBLK;
+    constexpr int NV = DBLK * (kBN / 16);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+        st.oacc[qb][i % DBLK] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], p_operand(pp[qb], i / DBLK), st.oacc[qb][i % DBLK], 0, 0, 0);
+    if (i + kVAhead < NV) vf[i + kVAhead] = v_fragment<D>(vt, st.voff[(i + kVAhead) % DBLK], (i + kVAhead) / DBLK);
+}
+
 // One pipelined step j (j + 1 < number of key tiles).  On entry pf holds the
 // fp32 probabilities of tile j (against the current references); on exit
-// those of tile j+1.  Work is split into two MFMA streams with independent
-// VALU work between their instructions:
+// those of tile j+1.  Two MFMA streams, each with independent VALU work in
+// its slots:
 //   scores:  S(j+1) = K(j+1) Q^T          || bf16 P(j) and its row sums
-//   values:  O += V(j)^T P(j)^T            || row max, exp2 of S(j+1)
+//   values:  O += V(j)^T P(j)^T            || row max (first DBLK slots),
+//                                             exp2 of S(j+1) (the rest)
 // plus the copies of K(j+2) and V(j+1) into the buffers read in step j-1.
 template <int D, int NW, int QB>
 __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)[QB][kBN / 32],
@@ -397,63 +439,79 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
                                               LDS_AS char* __restrict__ v_fill, const bf16* kbase, const bf16* vbase,
                                               size_t row_stride, int j, int n, float c, int wave, int lane) {
     constexpr int DBLK = WaveState<D, QB>::DBLK;
-    constexpr int KSTEPS = WaveState<D, QB>::KSTEPS;
+    constexpr int NV = DBLK * (kBN / 16);
+    constexpr int NE = NV - DBLK;                    // exp slots
+    constexpr int EPS = (QB * kBN / 2 + NE - 1) / NE;  // exp2 per exp slot (the last ones may take fewer)
     // keep the per-lane bases opaque to loop-invariant code motion: offsets
     // derived from them by XOR / add with constants are cheaper to recompute
     // each step than to hold in registers across the loop
     asm volatile("" : "+v"(st.koff0), "+v"(st.kcopy), "+v"(st.vcopy));
     const int h = lane >> 5;
     apply_pending_rescale(st);
-    if ((j + 2) * kBN < n) copy_tile<D, NW, false>(st.kcopy, kbase, row_stride, (j + 2) * kBN, n, k_fill, wave, lane);
-    if ((j + 1) * kBN < n) copy_tile<D, NW, true>(st.vcopy, vbase, row_stride, (j + 1) * kBN, n, v_fill, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
+    const TileJob<D, NW, false> kjob(st.kcopy, kbase, row_stride, (j + 2) * kBN, n, k_fill);
+    const TileJob<D, NW, true> vjob(st.vcopy, vbase, row_stride, (j + 1) * kBN, n, v_fill);
+    slot_fence();
     // scores stream
-    bf16x8 pb[QB][kBN / 16];
-    f32x16 s[QB][kBN / 32];
-    tile_scores(st, k_next, s);
-    tile_pack(st, pf, pb);
-    bf16x8 vf[kAhead];
-    tile_pv_begin(st, v_cur, vf);
-    // the bf16 probabilities and their sums are needed here, not only after
-    // the mask below
+    PackedP pp[QB];
+    float rs[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-        asm volatile("" ::"v"(pb[qb][0]), "v"(pb[qb][1]), "v"(pb[qb][2]), "v"(pb[qb][3]), "v"(st.l_run[qb]));
-    interleave_mfma<(kBN / 32) * KSTEPS, 2, QB, 1, 4 * QB>();
-    __builtin_amdgcn_sched_barrier(0);
+    for (int qb = 0; qb < QB; ++qb) rs[qb] = 0.f;
+    f32x16 s[QB][kBN / 32];
+    bf16x8 vf[NV];
+    score_slots<D, NW, QB, true>(st, k_next, v_cur, s, vf, pf, pp, rs, kjob, vjob, wave);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += rs[qb];
     const int lim = n - (j + 1) * kBN;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mask_tail(s[qb], lim, h);
-    __builtin_amdgcn_sched_barrier(0);
-    // values stream, part A: first 16 keys with the row maxes of S(j+1)
-    tile_pv<D, QB, 0, DBLK>(st, v_cur, pb, vf);
+    slot_fence();
+    // values stream, first DBLK slots: row maxes of S(j+1), a quarter of the
+    // scores per slot
     float mx[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) {
+        value_slot(st, v_cur, pp, vf, i);
+        constexpr int PER = 32 / DBLK;  // scores of each 32-key block per slot
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = i * PER; r < (i + 1) * PER; r += 2)
+                mx[qb] = fmaxf(fmaxf(mx[qb], fmaxf(s[qb][0][r], s[qb][0][r + 1])), fmaxf(s[qb][1][r], s[qb][1][r + 1]));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) pin(mx[qb]);
+        slot_fence();
+    }
     bool grow[QB];
     bool any_grow = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        mx[qb] = tile_max(s[qb]);
+        mx[qb] = pair_max(mx[qb]);
         grow[qb] = (mx[qb] - st.m_ref[qb]) * c > kRescaleLog2;
         any_grow |= grow[qb];
     }
-    const bool rescale = __builtin_amdgcn_ballot_w64(any_grow) != 0;
-    interleave_mfma<DBLK, 0, QB, 2, 6 * QB>();
-    __builtin_amdgcn_sched_barrier(0);
-    if (rescale) {
+    if (__builtin_amdgcn_ballot_w64(any_grow) != 0) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) st.alpha[qb] = move_reference(st, qb, mx[qb], grow[qb], c);
         st.pending = true;
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // values stream, part B: the remaining 48 keys with exp2 of S(j+1)
-    tile_pv<D, QB, DBLK, DBLK*(kBN / 16)>(st, v_cur, pb, vf);
+    slot_fence();
+    // values stream, remaining slots: exp2 of S(j+1), EPS scores per slot
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) tile_exp(s[qb], c, st.mc[qb]);
-    // the probabilities are needed here, not only in the next step
+    for (int i = DBLK; i < NV; ++i) {
+        value_slot(st, v_cur, pp, vf, i);
+        const int e0 = (i - DBLK) * EPS;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) asm volatile("" ::"v"(s[qb][0]), "v"(s[qb][1]));
-    interleave_mfma<DBLK*(kBN / 16 - 1), 0, QB, 2, 6 * QB>();
-    __builtin_amdgcn_sched_barrier(0);
+        for (int e = e0; e < e0 + EPS; ++e) {
+            if (e < QB * kBN / 2) {
+                const int qb = e / (kBN / 2), kb = (e / 16) % 2, r = e % 16;
+                s[qb][kb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], c, -st.mc[qb]));
+                pin(s[qb][kb][r]);
+            }
+        }
+        slot_fence();
+    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -465,12 +523,25 @@ template <int D, int QB>
 __device__ __forceinline__ void final_pv(WaveState<D, QB>& st, const f32x16 (&pf)[QB][kBN / 32],
                                          const LDS_AS char* __restrict__ v_cur) {
     constexpr int DBLK = WaveState<D, QB>::DBLK;
+    constexpr int NV = DBLK * (kBN / 16);
     apply_pending_rescale(st);
-    bf16x8 pb[QB][kBN / 16];
-    tile_pack(st, pf, pb);
-    bf16x8 vf[kAhead];
-    tile_pv_begin(st, v_cur, vf);
-    tile_pv<D, QB, 0, DBLK*(kBN / 16)>(st, v_cur, pb, vf);
+    PackedP pp[QB];
+    float rs[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) rs[qb] = 0.f;
+    bf16x8 vf[NV];
+#pragma unroll
+    for (int i = 0; i < kVAhead; ++i) vf[i] = v_fragment<D>(v_cur, st.voff[i % DBLK], i / DBLK);
+#pragma unroll
+    for (int i = 0; i < kBN / 4; ++i) pack_piece<QB>(pf, pp, rs, i);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += rs[qb];
+    slot_fence();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        value_slot(st, v_cur, pp, vf, i);
+        slot_fence();
+    }
 }
 
 // Waves per SIMD the register budget is sized for: one query block per wave
@@ -525,8 +596,21 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     st.kcopy = TileCopy<D, NW, false>::src_off0(row_stride, wave, lane);
     st.vcopy = TileCopy<D, NW, true>::src_off0(row_stride, wave, lane);
     const int nkv = (n + kBN - 1) / kBN;
-    copy_tile<D, NW, false>(st.kcopy, kbase, row_stride, 0, n, k0, wave, lane);
-    copy_tile<D, NW, true>(st.vcopy, vbase, row_stride, 0, n, v0, wave, lane);
+    // V rows past the window end are never loaded: the V buffers start as
+    // zeros (each wave clears the segments its own copies write, and waits for
+    // that before they are issued)
+    {
+        constexpr int VSEG = TileCopy<D, NW, true>::kPerWave;
+        typedef uint32_t u32x4z __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int i = 0; i < VSEG; ++i) {
+            *(LDS_AS u32x4z*)(v0 + (wave * VSEG + i) * 1024 + lane * 16) = u32x4z{0, 0, 0, 0};
+            *(LDS_AS u32x4z*)(v1 + (wave * VSEG + i) * 1024 + lane * 16) = u32x4z{0, 0, 0, 0};
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    }
+    TileJob<D, NW, false>(st.kcopy, kbase, row_stride, 0, n, k0).issue_all(wave);
+    TileJob<D, NW, true>(st.vcopy, vbase, row_stride, 0, n, v0).issue_all(wave);
 
     // query row of this lane in block qb: q0 + (wave * QB + qb) * 32 + lane % 32
     const int qrow0 = q0 + wave * 32 * QB + (lane & 31);
@@ -573,9 +657,17 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     // ---- prologue: tile 0 scores and probabilities ---------------------------
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile 0 have landed
     __syncthreads();                      // ... and every wave's
-    if (kBN < n) copy_tile<D, NW, false>(st.kcopy, kbase, row_stride, kBN, n, k1, wave, lane);
+    TileJob<D, NW, false>(st.kcopy, kbase, row_stride, kBN, n, k1).issue_all(wave);
     f32x16 pf[QB][kBN / 32];
-    tile_scores(st, k0, pf);
+    {
+        bf16x8 vf_unused[DBLK * (kBN / 16)];
+        PackedP pp_unused[QB];
+        float rs_unused[QB];
+        const TileJob<D, NW, false> kj_unused(st.kcopy, kbase, row_stride, 0, 0, k1);
+        const TileJob<D, NW, true> vj_unused(st.vcopy, vbase, row_stride, 0, 0, v1);
+        score_slots<D, NW, QB, false>(st, k0, k0, pf, vf_unused, pf, pp_unused, rs_unused, kj_unused, vj_unused,
+                                      wave);
+    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         mask_tail(pf[qb], n, h);
@@ -676,6 +768,8 @@ extern "C" int win_attn_fwd(const void* q, const void* k, const void* v, void* o
     if (lse && overlaps(lse, (uint64_t)batch * heads * L * 4, o, bytes)) return WIN_EINVAL;
     const int64_t pairs = (int64_t)batch * num_windows * heads;
     if (pairs >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
+    // a key tile's rows are addressed with 32-bit buffer offsets
+    if ((int64_t)kBN * heads * head_dim * 2 >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
     if (num_windows == 0 || L == 0 || max_seqlen == 0) return WIN_OK;
 
     AttnParams p;
