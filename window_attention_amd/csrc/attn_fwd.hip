@@ -290,9 +290,11 @@ __device__ __forceinline__ void tile_exp(f32x16 (&s)[kBN / 32], float c, float m
 }
 
 // bf16 probabilities (B operands of the P V product, one per 16 keys) and
-// their row sums, split into kBN / 4 pieces of one bf16 pair each: piece i
-// converts keys 2i, 2i+1 of fragment i / 4 and adds them to the row sum, so
-// a sum adds exactly the rounded weights the P V product uses.
+// their row sums, split into kBN / 4 pieces of one pair each: piece i
+// converts keys 2i, 2i+1 of fragment i / 4 and adds their fp32 values to the
+// row sum.  (Plain fp32 adds co-issue with the MFMAs; the packed bf16 dot
+// product that would add the rounded values instead shares their pipe.  The
+// two sums differ by at most 2^-9 relative per term.)
 struct PackedP {
     uint32_t w[kBN / 16][4];  // bf16 pairs of the B operand of 16-key step jj
 };
@@ -300,7 +302,6 @@ struct PackedP {
 template <int QB>
 __device__ __forceinline__ void pack_piece(const f32x16 (&pf)[QB][kBN / 32], PackedP (&pp)[QB], float (&rs)[QB],
                                            int i) {
-    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
     const int jj = i >> 2, m = i & 3;
     const int kb = jj >> 1, r = 8 * (jj & 1) + 2 * m;
 #pragma unroll
@@ -308,7 +309,8 @@ __device__ __forceinline__ void pack_piece(const f32x16 (&pf)[QB][kBN / 32], Pac
         const f32x2 x = {pf[qb][kb][r], pf[qb][kb][r + 1]};
         const bf16x2 pr = __builtin_convertvector(x, bf16x2);
         pp[qb].w[jj][m] = __builtin_bit_cast(uint32_t, pr);
-        rs[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs[qb], false);
+        rs[qb] += x[0];
+        rs[qb] += x[1];
         pin(pp[qb].w[jj][m]);
         pin(rs[qb]);
     }
@@ -473,27 +475,32 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
 #pragma unroll
     for (int i = 0; i < DBLK; ++i) {
         value_slot(st, v_cur, pp, vf, i);
-        constexpr int PER = 32 / DBLK;  // scores of each 32-key block per slot
+        constexpr int PER = 16 / DBLK;  // accumulator rows of each 32-key block per slot
+        static_assert(PER * DBLK == 16, "the row max must split evenly over the first value slots");
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int r = i * PER; r < (i + 1) * PER; r += 2)
-                mx[qb] = fmaxf(fmaxf(mx[qb], fmaxf(s[qb][0][r], s[qb][0][r + 1])), fmaxf(s[qb][1][r], s[qb][1][r + 1]));
+            for (int r = i * PER; r < (i + 1) * PER; ++r)
+                mx[qb] = fmaxf(fmaxf(mx[qb], s[qb][0][r]), s[qb][1][r]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) pin(mx[qb]);
         slot_fence();
     }
-    bool grow[QB];
+    // The reference moves only when some lane's own 32 scores exceed it by
+    // more than kRescaleLog2 (base 2): the lane pair of a query shares one
+    // reference, and each lane's probabilities stay below 2^kRescaleLog2 as
+    // long as its own maximum does.  The exact pair maximum, the one exchange
+    // between the two lanes, is only needed on that rare path.
     bool any_grow = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        mx[qb] = pair_max(mx[qb]);
-        grow[qb] = (mx[qb] - st.m_ref[qb]) * c > kRescaleLog2;
-        any_grow |= grow[qb];
-    }
+    for (int qb = 0; qb < QB; ++qb) any_grow |= (mx[qb] - st.m_ref[qb]) * c > kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(any_grow) != 0) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) st.alpha[qb] = move_reference(st, qb, mx[qb], grow[qb], c);
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mxp = pair_max(mx[qb]);
+            const bool grow = (mxp - st.m_ref[qb]) * c > kRescaleLog2;  // equal in both lanes of the pair
+            st.alpha[qb] = move_reference(st, qb, mxp, grow, c);
+        }
         st.pending = true;
     }
     slot_fence();
