@@ -525,6 +525,16 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
         for (int kb = 0; kb < kBN / 32; ++kb) pf[qb][kb] = s[qb][kb];
 }
 
+// Step j of a wave with no query row inside the window: only its share of
+// the tile copies (the LDS tiles are shared by the workgroup).
+template <int D, int NW, int QB>
+__device__ __forceinline__ void copy_step(const WaveState<D, QB>& st, LDS_AS char* __restrict__ k_fill,
+                                          LDS_AS char* __restrict__ v_fill, const bf16* kbase, const bf16* vbase,
+                                          size_t row_stride, int j, int n, int wave) {
+    TileJob<D, NW, false>(st.kcopy, kbase, row_stride, (j + 2) * kBN, n, k_fill).issue_all(wave);
+    TileJob<D, NW, true>(st.vcopy, vbase, row_stride, (j + 1) * kBN, n, v_fill).issue_all(wave);
+}
+
 // P V product of the last tile, whose probabilities are in pf.
 template <int D, int QB>
 __device__ __forceinline__ void final_pv(WaveState<D, QB>& st, const f32x16 (&pf)[QB][kBN / 32],
@@ -665,8 +675,12 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile 0 have landed
     __syncthreads();                      // ... and every wave's
     TileJob<D, NW, false>(st.kcopy, kbase, row_stride, kBN, n, k1).issue_all(wave);
+    // A wave whose query rows all lie past the window end (the last query
+    // tile of a window) computes nothing; it still copies its share of every
+    // tile and meets every barrier.
+    const bool active = q0 + wave * 32 * QB < n;
     f32x16 pf[QB][kBN / 32];
-    {
+    if (active) {
         bf16x8 vf_unused[DBLK * (kBN / 16)];
         PackedP pp_unused[QB];
         float rs_unused[QB];
@@ -674,12 +688,12 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
         const TileJob<D, NW, true> vj_unused(st.vcopy, vbase, row_stride, 0, 0, v1);
         score_slots<D, NW, QB, false>(st, k0, k0, pf, vf_unused, pf, pp_unused, rs_unused, kj_unused, vj_unused,
                                       wave);
-    }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        mask_tail(pf[qb], n, h);
-        move_reference(st, qb, tile_max(pf[qb]), true, c);  // first reference: the tile max (O is still zero)
-        tile_exp(pf[qb], c, st.mc[qb]);
+        for (int qb = 0; qb < QB; ++qb) {
+            mask_tail(pf[qb], n, h);
+            move_reference(st, qb, tile_max(pf[qb]), true, c);  // first reference: the tile max (O is still zero)
+            tile_exp(pf[qb], c, st.mc[qb]);
+        }
     }
 
     // ---- pipelined key loop, steps in pairs so that LDS buffers are static ----
@@ -690,21 +704,31 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     for (; j + 2 < nkv; j += 2) {
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        pipeline_step<D, NW, QB>(st, pf, k1, v0, k0, v1, kbase, vbase, row_stride, j, n, c, wave, lane);
+        if (active)
+            pipeline_step<D, NW, QB>(st, pf, k1, v0, k0, v1, kbase, vbase, row_stride, j, n, c, wave, lane);
+        else
+            copy_step<D, NW, QB>(st, k0, v1, kbase, vbase, row_stride, j, n, wave);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        pipeline_step<D, NW, QB>(st, pf, k0, v1, k1, v0, kbase, vbase, row_stride, j + 1, n, c, wave, lane);
+        if (active)
+            pipeline_step<D, NW, QB>(st, pf, k0, v1, k1, v0, kbase, vbase, row_stride, j + 1, n, c, wave, lane);
+        else
+            copy_step<D, NW, QB>(st, k1, v0, kbase, vbase, row_stride, j + 1, n, wave);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (j + 1 < nkv) {  // one more full step (tiles j, j+1), then the P V of tile j+1
-        pipeline_step<D, NW, QB>(st, pf, k1, v0, k0, v1, kbase, vbase, row_stride, j, n, c, wave, lane);
+        if (active)
+            pipeline_step<D, NW, QB>(st, pf, k1, v0, k0, v1, kbase, vbase, row_stride, j, n, c, wave, lane);
+        else
+            copy_step<D, NW, QB>(st, k0, v1, kbase, vbase, row_stride, j, n, wave);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        final_pv(st, pf, v1);
-    } else {  // the P V of tile j
+        if (active) final_pv(st, pf, v1);
+    } else if (active) {  // the P V of tile j
         final_pv(st, pf, v0);
     }
+    if (!active) return;
 
     // ---- epilogue ------------------------------------------------------------
 #pragma unroll
