@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default="video_21x45x80")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the practical-ceiling measurements (vendor GEMM and plain copy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain device-to-device copy of one workload tensor (the reference kernel of "
                          "known size for HBM byte counters)")
@@ -139,6 +141,41 @@ def measured_traffic(kernel_prefix, workload):
         return {"fetch_bytes": int(rec["fetch_bytes"]), "write_bytes": int(rec["write_bytes"]),
                 "total_bytes": int(rec["fetch_bytes"]) + int(rec["write_bytes"])}
     return None
+
+
+def practical_ceilings(torch, w, reps=20):
+    """What this machine sustains, measured here beside the path (context only, not
+    part of it): a vendor dense bf16 GEMM on N(0,1) data, whose power-limited
+    clock is the practical ceiling of an MFMA-bound kernel on real data, and a
+    plain device copy of one workload-sized tensor, the practical ceiling of a
+    permute."""
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = torch.empty_like(a)
+    for _ in range(3):
+        torch.matmul(a, a, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, a, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tfs = 2 * n ** 3 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+    del a, c
+    x = torch.empty((w.batch, w.L, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * x.numel() * 2 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    return {"gemm_bf16_tflops": round(gemm_tfs, 1), "gemm": f"torch.matmul bf16 {n}x{n}x{n}, N(0,1) data",
+            "copy_gbps": round(copy_gbs, 1), "copy": f"device copy of {x.numel() * 2} bytes"}
 
 
 def cpu_baseline(w, seconds):
@@ -292,6 +329,14 @@ def main():
                              "avg_launch_ms": round(sum(perm_ms) / len(perm_ms), 4),
                              "bytes_per_launch": perm_bytes_launch},
     }
+    if not args.no_ceilings:
+        ceil = practical_ceilings(torch, w)
+        ceil["attn_frac_of_gemm"] = round(attn_tfs / ceil["gemm_bf16_tflops"], 4)
+        ceil["permute_frac_of_copy"] = round(perm_gbs / ceil["copy_gbps"], 4)
+        log(f"[bench] practical ceilings: vendor bf16 GEMM {ceil['gemm_bf16_tflops']} TFLOP/s "
+            f"(attention at {ceil['attn_frac_of_gemm']:.2f} of it), device copy {ceil['copy_gbps']} GB/s "
+            f"(permutes at {ceil['permute_frac_of_copy']:.2f} of it)")
+        res["practical_ceilings"] = ceil
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle sample, about {args.cpu_seconds:.0f} s")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
