@@ -16,5 +16,7 @@ permute    entry gather, exit scatter and layout-to-layout transition
 attention  per-window softmax attention in fp64, and the brute-force twin that
            runs full attention under a same-window mask (section "Motivation",
            "SeedVR2 integration").
+pack       several requests' plans packed into one varlen call with alignment
+           tails (page "vLLM-Omni diffusion runtime", section 4.2).
 """
-from . import plan, permute, attention  # noqa: F401
+from . import plan, permute, attention, pack  # noqa: F401

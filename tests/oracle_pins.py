@@ -174,6 +174,58 @@ def check_shift_geometry(oracle_plan, n, w):
         assert sh != reg
 
 
+# ----------------------------------------------------------------- packing pins
+
+def check_pack_worked_example(pack_fn):
+    """The page's teaching layout (tests/golden/pack_worked_example.json):
+    ``pack_fn(perms, cus, align)`` returns (offsets, perm, cu_seqlens,
+    max_seqlen)."""
+    g = load_golden("pack_worked_example.json")
+    perms = [list(range(r["rows"])) for r in g["requests"]]
+    cus = [r["cu_seqlens"] for r in g["requests"]]
+    offsets, perm, cu, mx = pack_fn(perms, cus, g["align"])
+    assert list(cu) == g["expected"]["cu_seqlens"]
+    assert mx == g["expected"]["max_seqlen"]
+    assert list(offsets) == g["expected"]["offsets"]
+    assert list(perm) == list(range(128))
+
+
+def check_pack_invariants(pack_fn, perms, cus, align):
+    """What the page fixes for any packing: requests back to back with
+    alignment tails; each request's windows and tail as separate segments
+    (the tail's boundary present even when it is empty); the physical index
+    shifted by the request's offset; max_seqlen the longest segment."""
+    offsets, perm, cu, mx = pack_fn(perms, cus, align)
+    offsets, perm, cu = list(offsets), list(perm), list(cu)
+    R = len(perms)
+    assert len(offsets) == R + 1 and offsets[0] == 0
+    total = offsets[-1]
+    assert len(perm) == total and sorted(perm) == list(range(total))
+    assert len(cu) == 1 + sum(len(c) - 1 for c in cus) + R
+    assert cu[0] == 0 and cu[-1] == total and all(a <= b for a, b in zip(cu, cu[1:]))
+    seg = 1
+    longest = 0
+    for r, (p, c) in enumerate(zip(perms, cus)):
+        o, n = offsets[r], len(p)
+        pad = offsets[r + 1] - o - n
+        assert o % align == 0 and 0 <= pad < align
+        # rows: the request's own gather table, moved by its offset
+        assert perm[o:o + n] == [o + x for x in p]
+        # tail: padding rows stay in place
+        assert perm[o + n:o + n + pad] == list(range(o + n, o + n + pad))
+        # segments: the request's windows, then its tail
+        for a, b in zip(c[:-1], c[1:]):
+            assert cu[seg] - cu[seg - 1] == b - a
+            assert cu[seg] == o + b
+            longest = max(longest, b - a)
+            seg += 1
+        assert cu[seg] == o + n + pad and cu[seg] - cu[seg - 1] == pad
+        longest = max(longest, pad)
+        seg += 1
+    assert seg == len(cu)
+    assert mx == longest
+
+
 # --------------------------------------------------------------- attention pins
 
 def torch_sdpa_masked(qc, kc, vc, window_of_token, scale):

@@ -222,3 +222,51 @@ def test_permute_mutant_is_caught(monkeypatch):
     p = oplan.plan(1, 3, 4, 1, 26, 35, oplan.REGULAR)
     x = np.arange(12)[None, :]
     assert not np.array_equal(operm.scatter(operm.gather(x, p.perm), p.perm), x)
+
+
+# ----------------------------------------------------------------- packing
+
+from oracle import pack as opack  # noqa: E402
+
+
+def _pack_pins_fail():
+    def fn(perms, cus, align):
+        k = opack.pack_plans(perms, cus, align)
+        return k.offsets, k.perm, k.cu_seqlens, k.max_seqlen
+    try:
+        pins.check_pack_worked_example(fn)
+        plans = [oplan.plan(5, 9, 16, 2, 6, 6, oplan.REGULAR), oplan.plan(2, 5, 7, 1, 2, 3, oplan.SHIFTED)]
+        for align in (1, 7, 64):
+            pins.check_pack_invariants(fn, [list(p.perm) for p in plans], [list(p.cu_seqlens) for p in plans], align)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def _pack_variant(skip_empty_tail=False, unshifted=False, full_tail=False, total_max=False):
+    def pack_plans(perms, cus, align):
+        offsets, perm, cu, longest = [0], [], [0], 0
+        for p, c in zip(perms, cus):
+            n, o = len(p), offsets[-1]
+            for a, b in zip(c[:-1], c[1:]):
+                cu.append(o + b)
+                longest = max(longest, b - a)
+            perm.extend(x if unshifted else o + x for x in p)
+            t = align - n % align if full_tail else (align - n % align) % align
+            perm.extend(range(o + n, o + n + t))
+            if t or not skip_empty_tail:
+                cu.append(o + n + t)
+            longest = max(longest, t)
+            offsets.append(o + n + t)
+        return opack.Packed(offsets, perm, cu, offsets[-1] if total_max else longest)
+    return pack_plans
+
+
+def test_unmutated_pack_passes():
+    assert not _pack_pins_fail()
+
+
+@pytest.mark.parametrize("flag", ["skip_empty_tail", "unshifted", "full_tail", "total_max"])
+def test_pack_mutant_is_caught(flag, monkeypatch):
+    monkeypatch.setattr(opack, "pack_plans", _pack_variant(**{flag: True}))
+    assert _pack_pins_fail(), f"pins did not catch packing mutant {flag}"
