@@ -17,6 +17,9 @@
  *   - win_attn_fwd    sections "Motivation" and "SeedVR2 integration":
  *                     attention only inside each window, one packed
  *                     variable-length call over cu_seqlens segments.
+ * and the page "vLLM-Omni diffusion runtime" (blog post):
+ *   - win_pack        section 4.2: several requests' plans packed into one
+ *                     varlen call with alignment tails.
  *
  * Conventions shared by every entry point
  *   - Every function returns WIN_OK (0) or a negative status; win_strerror()
@@ -156,6 +159,36 @@ int win_transition(const void* src, void* dst, const int32_t* inv_src, const int
 int win_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                  int32_t num_windows, int32_t max_seqlen, int64_t L, int32_t batch, int32_t heads,
                  int32_t head_dim, float softmax_scale, void* stream);
+
+/*
+ * Packing of several requests' plans into one varlen call (page "vLLM-Omni
+ * diffusion runtime", section 4.2 on packing).  Request r (r = 0..R-1, in
+ * order) occupies rows [offsets[r], offsets[r] + L_r) of the packed token
+ * tensor, followed by an alignment tail of (align - L_r % align) % align rows;
+ * offsets[r+1] = offsets[r] + L_r + tail.
+ *   cu_out:   the request's window boundaries moved by offsets[r], then the
+ *             end of its tail, for every request in order after a leading 0:
+ *             sum(N_r) + R segments; a zero-length tail repeats a boundary.
+ *   perm_out: perm_out[offsets[r] + j] = offsets[r] + perm_r[j]; tail rows map
+ *             to themselves.  Use it with win_permute on the packed tensor;
+ *             positional coordinates stay request-local.
+ *   max_seqlen: the longest segment (windows and tails).
+ * Arguments (all host memory)
+ *   num_requests R > 0; num_tokens[R] (L_r > 0); num_windows[R] (N_r > 0);
+ *   perms       the R perm tables back to back (sum L_r int32), NULL only if
+ *               perm_out is NULL;
+ *   cu_seqlens  the R cu_seqlens tables back to back (sum (N_r + 1) int32);
+ *   align > 0;
+ *   offsets     out, R + 1 int64;  perm_out out (total rows int32) or NULL;
+ *   cu_out      out, sum(N_r) + R + 1 int32;  max_seqlen out, required.
+ * Errors: WIN_EINVAL (a table that is not a plan: cu not starting at 0, not
+ * ending at L_r or decreasing, a perm entry outside [0, L_r); null or
+ * non-positive arguments), WIN_EOVERFLOW (L_r or the packed rows >= 2^31).
+ * Nothing is written unless the call succeeds.
+ */
+int win_pack(int32_t num_requests, const int64_t* num_tokens, const int32_t* num_windows, const int32_t* perms,
+             const int32_t* cu_seqlens, int32_t align, int64_t* offsets, int32_t* perm_out, int32_t* cu_out,
+             int32_t* max_seqlen);
 
 /* Static string naming a status code. */
 const char* win_strerror(int status);

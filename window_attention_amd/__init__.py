@@ -10,6 +10,7 @@ memory and the current stream.  The C entry points are documented in
     scatter()     -> win_permute(mode=WIN_SCATTER)
     transition()  -> win_transition
     attn_fwd()    -> win_attn_fwd
+    pack()        -> win_pack
 
 If the library has not been built the first call raises ``WinAttnError``;
 there is no fallback implementation.
@@ -22,8 +23,8 @@ import os
 from collections import OrderedDict
 from dataclasses import dataclass
 
-__all__ = ["WinAttnError", "Plan", "plan", "plan_cached", "gather", "scatter", "transition", "attn_fwd",
-           "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
+__all__ = ["WinAttnError", "Plan", "Packed", "plan", "plan_cached", "pack", "gather", "scatter", "transition",
+           "attn_fwd", "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
 
 REGULAR = 0
 SHIFTED = 1
@@ -66,6 +67,8 @@ def load_library():
     lib.win_transition.restype = ctypes.c_int
     lib.win_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, vp]
     lib.win_attn_fwd.restype = ctypes.c_int
+    lib.win_pack.argtypes = [i32, vp, vp, vp, vp, i32, vp, vp, vp, ctypes.POINTER(i32)]
+    lib.win_pack.restype = ctypes.c_int
     lib.win_strerror.argtypes = [ctypes.c_int]
     lib.win_strerror.restype = ctypes.c_char_p
     lib.win_build_info.argtypes = []
@@ -172,6 +175,43 @@ def plan_cached(T, H, W, nt, nh, nw, method=REGULAR, device=None) -> Plan:
     while len(_PLAN_CACHE) > PLAN_CACHE_SIZE:
         _PLAN_CACHE.popitem(last=False)
     return p
+
+
+@dataclass
+class Packed:
+    """Several requests' plans as one varlen call (see ``win_pack`` in
+    include/winattn.h): request r owns rows ``offsets[r] .. offsets[r+1]-1``
+    of the packed token tensor (its rows, then its alignment tail)."""
+    offsets: list
+    num_tokens: int     # packed rows, tails included
+    num_windows: int    # segments of the packed call (windows and tails)
+    max_seqlen: int
+    perm: object        # torch.int32 [num_tokens]
+    cu_seqlens: object  # torch.int32 [num_windows + 1]
+
+
+def pack(plans, align=64, device=None) -> Packed:
+    """Pack ``plans`` (in request order) into one varlen call; tables are
+    returned on ``device`` (None: host)."""
+    import torch
+    lib = load_library()
+    R = len(plans)
+    if R == 0:
+        raise WinAttnError(-1, "pack needs at least one plan")
+    toks = (ctypes.c_int64 * R)(*[p.num_tokens for p in plans])
+    nwin = (ctypes.c_int32 * R)(*[p.num_windows for p in plans])
+    perms = torch.cat([p.perm.cpu() for p in plans]).contiguous()
+    cus = torch.cat([p.cu_seqlens.cpu() for p in plans]).contiguous()
+    offsets = (ctypes.c_int64 * (R + 1))()
+    total_max = sum(p.num_tokens + align for p in plans)
+    perm_out = torch.empty(total_max, dtype=torch.int32)
+    cu_out = torch.empty(sum(p.num_windows for p in plans) + R + 1, dtype=torch.int32)
+    mx = ctypes.c_int32()
+    _check(lib.win_pack(R, toks, nwin, _ptr(perms), _ptr(cus), int(align), offsets, _ptr(perm_out), _ptr(cu_out),
+                        ctypes.byref(mx)), "win_pack")
+    total = offsets[R]
+    dev = torch.device("cpu") if device is None else torch.device(device)
+    return Packed(list(offsets), total, cu_out.numel() - 1, mx.value, perm_out[:total].to(dev), cu_out.to(dev))
 
 
 def _rows(x):

@@ -133,3 +133,62 @@ extern "C" int win_plan(int32_t T, int32_t H, int32_t W, int32_t nt, int32_t nh,
     }
     return WIN_OK;
 }
+
+// win_pack: several requests' window plans packed into one varlen call (page
+// "vLLM-Omni diffusion runtime", section 4.2 on packing): request r's rows
+// follow those of the requests before it, padded by an alignment tail; its
+// windows, moved by its row offset, and then its tail are segments of their
+// own (a zero-length tail keeps its repeated boundary); the gather index of a
+// row gets the request's offset added, and tail rows stay in place.  Host
+// integer work: everything is validated before anything is written.
+extern "C" int win_pack(int32_t num_requests, const int64_t* num_tokens, const int32_t* num_windows,
+                        const int32_t* perms, const int32_t* cu_seqlens, int32_t align, int64_t* offsets,
+                        int32_t* perm_out, int32_t* cu_out, int32_t* max_seqlen) {
+    if (num_requests <= 0 || !num_tokens || !num_windows || !cu_seqlens || align <= 0) return WIN_EINVAL;
+    if (!offsets || !cu_out || !max_seqlen || (perm_out && !perms)) return WIN_EINVAL;
+    int64_t total = 0, longest = 0;
+    const int32_t* c = cu_seqlens;
+    const int32_t* p = perms;
+    for (int32_t r = 0; r < num_requests; ++r) {
+        const int64_t L = num_tokens[r];
+        const int32_t N = num_windows[r];
+        if (L <= 0 || N <= 0 || L >= ((int64_t)1 << 31)) return L >= ((int64_t)1 << 31) ? WIN_EOVERFLOW : WIN_EINVAL;
+        if (c[0] != 0 || c[N] != L) return WIN_EINVAL;
+        for (int32_t i = 0; i < N; ++i) {
+            if (c[i + 1] < c[i]) return WIN_EINVAL;
+            longest = c[i + 1] - c[i] > longest ? c[i + 1] - c[i] : longest;
+        }
+        if (perm_out) {
+            for (int64_t j = 0; j < L; ++j)
+                if (p[j] < 0 || p[j] >= L) return WIN_EINVAL;
+            p += L;
+        }
+        const int64_t pad = (align - L % align) % align;
+        longest = pad > longest ? pad : longest;
+        total += L + pad;
+        if (total >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
+        c += N + 1;
+    }
+    c = cu_seqlens;
+    p = perms;
+    int64_t k = 0, o = 0;
+    cu_out[k++] = 0;
+    for (int32_t r = 0; r < num_requests; ++r) {
+        const int64_t L = num_tokens[r];
+        const int32_t N = num_windows[r];
+        const int64_t end = o + L + (align - L % align) % align;
+        offsets[r] = o;
+        for (int32_t i = 1; i <= N; ++i) cu_out[k++] = (int32_t)(o + c[i]);
+        cu_out[k++] = (int32_t)end;
+        if (perm_out) {
+            for (int64_t j = 0; j < L; ++j) perm_out[o + j] = (int32_t)(o + p[j]);
+            for (int64_t t = o + L; t < end; ++t) perm_out[t] = (int32_t)t;
+            p += L;
+        }
+        c += N + 1;
+        o = end;
+    }
+    offsets[num_requests] = o;
+    *max_seqlen = (int32_t)longest;
+    return WIN_OK;
+}
