@@ -18,5 +18,8 @@ attention  per-window softmax attention in fp64, and the brute-force twin that
            "SeedVR2 integration").
 pack       several requests' plans packed into one varlen call with alignment
            tails (page "vLLM-Omni diffusion runtime", section 4.2).
+sp_plan    the single-GPU tables of window-aligned sequence parallelism: LPT
+           assignment and Plan A redistribution, with the exchange simulated
+           on fake ranks (sections "Planner", "Plan A redistribution").
 """
-from . import plan, permute, attention, pack  # noqa: F401
+from . import plan, permute, attention, pack, sp_plan  # noqa: F401

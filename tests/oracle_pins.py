@@ -226,6 +226,75 @@ def check_pack_invariants(pack_fn, perms, cus, align):
     assert mx == longest
 
 
+# ------------------------------------------------------- sequence-parallel pins
+
+def check_lpt_worked_examples(lpt_fn):
+    """Hand-derived LPT assignments (tests/golden/sp_plan_worked_example.json):
+    ``lpt_fn(sizes, ranks)`` returns (owner, lists, loads)."""
+    g = load_golden("sp_plan_worked_example.json")
+    for e in g["lpt"]:
+        owner, lists, loads = lpt_fn(e["sizes"], e["ranks"])
+        assert list(owner) == e["owner"] and [list(x) for x in lists] == e["lists"] and list(loads) == e["loads"]
+
+
+def check_lpt_invariants(lpt_fn, sizes, ranks):
+    """A partition of the windows, each rank's list ascending, loads summing
+    the sizes, and the bound every greedy list schedule meets: no rank holds
+    more than the mean load plus the largest window."""
+    owner, lists, loads = lpt_fn(sizes, ranks)
+    assert sorted(w for ws in lists for w in ws) == list(range(len(sizes)))
+    for r, ws in enumerate(lists):
+        assert list(ws) == sorted(ws) and all(owner[w] == r for w in ws)
+        assert loads[r] == sum(sizes[w] for w in ws)
+    if sizes:
+        assert max(loads) <= sum(sizes) / ranks + max(sizes)
+
+
+def check_plan_a_worked_example(plan_a_fn):
+    """The hand-derived two-rank exchange on the 3x4 grid, regular to shifted:
+    ``plan_a_fn(z_src, z_dst)`` returns (counts, send_rows, recv_pos,
+    exchange_required)."""
+    e = load_golden("sp_plan_worked_example.json")["plan_a"]
+    counts, send, recv, ex = plan_a_fn(e["z_src"], e["z_dst"])
+    assert [list(x) for x in counts] == e["counts"]
+    assert [list(x) for x in send] == e["send_rows"] and [list(x) for x in recv] == e["recv_pos"]
+    assert bool(ex) == e["exchange_required"]
+
+
+def check_plan_a_invariants(plan_a_fn, z_src, z_dst):
+    """The exchange the tables drive (simulated with lists for the ranks'
+    buffers) turns every source holding into the destination holding; split
+    sizes are the row and column of the count matrix; each peer segment
+    arrives in destination-local order; the exchange flag is global."""
+    counts, send, recv, ex = plan_a_fn(z_src, z_dst)
+    P = len(z_src)
+    assert [sum(counts[r]) for r in range(P)] == [len(z) for z in z_src]
+    assert [sum(counts[r][d] for r in range(P)) for d in range(P)] == [len(z) for z in z_dst]
+    for d in range(P):
+        k = 0
+        for r in range(P):
+            seg = list(recv[d][k:k + counts[r][d]])
+            assert seg == sorted(seg)          # destination-local order within each peer segment
+            k += counts[r][d]
+        assert sorted(recv[d]) == list(range(len(z_dst[d])))
+    # simulated all-to-all: rank r's rows are its canonical ids
+    outbox = []
+    for r in range(P):
+        rows = [z_src[r][i] for i in send[r]]
+        segs, k = [], 0
+        for d in range(P):
+            segs.append(rows[k:k + counts[r][d]])
+            k += counts[r][d]
+        outbox.append(segs)
+    for d in range(P):
+        got = [row for r in range(P) for row in outbox[r][d]]
+        placed = [None] * len(got)
+        for t, pos in enumerate(recv[d]):
+            placed[pos] = got[t]
+        assert placed == list(z_dst[d])
+    assert bool(ex) == any(counts[r][d] for r in range(P) for d in range(P) if r != d)
+
+
 # --------------------------------------------------------------- attention pins
 
 def torch_sdpa_masked(qc, kc, vc, window_of_token, scale):

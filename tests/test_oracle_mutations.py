@@ -270,3 +270,70 @@ def test_unmutated_pack_passes():
 def test_pack_mutant_is_caught(flag, monkeypatch):
     monkeypatch.setattr(opack, "pack_plans", _pack_variant(**{flag: True}))
     assert _pack_pins_fail(), f"pins did not catch packing mutant {flag}"
+
+
+# ------------------------------------------------------- sequence-parallel tables
+
+from oracle import sp_plan as osp  # noqa: E402
+
+
+def _sp_pins_fail():
+    try:
+        pins.check_lpt_worked_examples(osp.lpt_assign)
+        pins.check_plan_a_worked_example(
+            lambda a, b: (lambda t: (t.counts, t.send_rows, t.recv_pos, t.exchange_required))(osp.plan_a(a, b)))
+        p = oplan.plan(5, 9, 16, 2, 6, 6, oplan.SHIFTED)
+        sizes = [p.cu_seqlens[i + 1] - p.cu_seqlens[i] for i in range(p.num_windows)]
+        for ranks in (2, 3):
+            pins.check_lpt_invariants(osp.lpt_assign, sizes, ranks)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def _lpt_variant(rank_tie_high=False, ascending=False, keep_lpt_order=False):
+    def lpt_assign(sizes, ranks):
+        order = sorted(range(len(sizes)), key=lambda w: ((sizes[w] if ascending else -sizes[w]), w))
+        load, owner, lists = [0] * ranks, [-1] * len(sizes), [[] for _ in range(ranks)]
+        for w in order:
+            r = min(range(ranks), key=lambda x: (load[x], -x if rank_tie_high else x))
+            owner[w] = r
+            load[r] += sizes[w]
+            lists[r].append(w)
+        if not keep_lpt_order:
+            lists = [sorted(x) for x in lists]
+        return owner, lists, load
+    return lpt_assign
+
+
+def _plan_a_source_order(z_src, z_dst):
+    # peer segments packed in source-local order instead of destination-local order
+    P = len(z_src)
+    where = {c: (d, pos) for d, z in enumerate(z_dst) for pos, c in enumerate(z)}
+    counts = [[0] * P for _ in range(P)]
+    send, recv_parts = [], [[[] for _ in range(P)] for _ in range(P)]
+    for r, z in enumerate(z_src):
+        groups = [[] for _ in range(P)]
+        for i, c in enumerate(z):
+            d, pos = where[c]
+            counts[r][d] += 1
+            groups[d].append(i)
+            recv_parts[d][r].append(pos)
+        send.append([i for g in groups for i in g])
+    recv = [[p for part in recv_parts[d] for p in part] for d in range(P)]
+    return osp.PlanA(counts, send, recv, any(counts[r][d] for r in range(P) for d in range(P) if r != d))
+
+
+def test_unmutated_sp_tables_pass():
+    assert not _sp_pins_fail()
+
+
+@pytest.mark.parametrize("flag", ["rank_tie_high", "ascending", "keep_lpt_order"])
+def test_lpt_mutant_is_caught(flag, monkeypatch):
+    monkeypatch.setattr(osp, "lpt_assign", _lpt_variant(**{flag: True}))
+    assert _sp_pins_fail(), f"pins did not catch LPT mutant {flag}"
+
+
+def test_plan_a_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(osp, "plan_a", _plan_a_source_order)
+    assert _sp_pins_fail(), "pins did not catch Plan A packed in source order"
