@@ -17,6 +17,9 @@
  *   - win_attn_fwd    sections "Motivation" and "SeedVR2 integration":
  *                     attention only inside each window, one packed
  *                     variable-length call over cu_seqlens segments.
+ *   - win_lpt,        sections "Planner" and "Plan A redistribution": the
+ *     win_plan_a      single-GPU tables of window-aligned sequence
+ *                     parallelism (window assignment, exchange tables).
  * and the page "vLLM-Omni diffusion runtime" (blog post):
  *   - win_pack        section 4.2: several requests' plans packed into one
  *                     varlen call with alignment tails.
@@ -189,6 +192,53 @@ int win_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 int win_pack(int32_t num_requests, const int64_t* num_tokens, const int32_t* num_windows, const int32_t* perms,
              const int32_t* cu_seqlens, int32_t align, int64_t* offsets, int32_t* perm_out, int32_t* cu_out,
              int32_t* max_seqlen);
+
+/*
+ * Deterministic LPT assignment of windows to `ranks` ranks (window page,
+ * section "Planner"): windows are taken by decreasing token count, ties by
+ * window id; each goes to the rank with the fewest assigned tokens, ties to
+ * the lower rank; each rank then lists its windows in ascending id.  This is
+ * what each rank of window-aligned sequence parallelism would own; with
+ * ranks = 1 every window is on rank 0.
+ * Arguments (host): num_windows N >= 0; cu_seqlens [N+1] (window sizes are
+ *   its differences); ranks > 0; owner [N] out (rank of each window);
+ *   order [N] out (windows grouped by rank, rank 0 first, ascending ids);
+ *   rank_offsets [ranks+1] out (rank r's windows are order[rank_offsets[r] ..
+ *   rank_offsets[r+1]-1]); rank_tokens [ranks] out (int64 tokens per rank).
+ * Errors: WIN_EINVAL (null pointer, cu not starting at 0 or decreasing).
+ */
+int win_lpt(int32_t num_windows, const int32_t* cu_seqlens, int32_t ranks, int32_t* owner, int32_t* order,
+            int32_t* rank_offsets, int64_t* rank_tokens);
+
+/*
+ * Plan A redistribution tables between a source and a destination layout,
+ * each with its window assignment (window page, section "Plan A
+ * redistribution").  Rank r holds, in its local order, the tokens of its
+ * windows in listed order (win_lpt's `order`), row-major inside each window
+ * (the plan's window order).
+ *   counts [ranks*ranks] int64 out, row-major: counts[r*ranks + d] = rows rank
+ *     d needs from rank r.  Rank r's input split sizes are row r, its output
+ *     split sizes column r.
+ *   send_rows [L] out: for each source rank r in turn (its block starts at its
+ *     first row in rank order), its local rows to send, grouped by destination
+ *     rank and, inside a group, in destination-local order.
+ *   recv_pos [L] out: for each destination rank d in turn, the
+ *     destination-local position of each row it receives, rows concatenated in
+ *     source-rank order; the receiver reorders with one argsort of these.
+ *   exchange_required out: 1 if some row changes rank (computed from the whole
+ *     count matrix, so every rank takes the same branch), else 0.
+ * With ranks = 1 this is the local transition: send_rows = inv_src[perm_dst].
+ * Arguments (host): L tokens (both layouts); the source plan's perm [L] and
+ *   cu_seqlens [src_windows+1] with its assignment (order, rank_offsets as
+ *   win_lpt returns them); the same for the destination.
+ * Errors: WIN_EINVAL (inconsistent tables: a perm that is not a permutation,
+ *   an assignment that is not a partition, bad cu), WIN_EOVERFLOW (L >= 2^31).
+ */
+int win_plan_a(int64_t L, int32_t ranks, const int32_t* src_perm, const int32_t* src_cu, int32_t src_windows,
+               const int32_t* src_order, const int32_t* src_rank_offsets, const int32_t* dst_perm,
+               const int32_t* dst_cu, int32_t dst_windows, const int32_t* dst_order,
+               const int32_t* dst_rank_offsets, int64_t* counts, int32_t* send_rows, int32_t* recv_pos,
+               int32_t* exchange_required);
 
 /* Static string naming a status code. */
 const char* win_strerror(int status);

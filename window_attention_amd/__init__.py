@@ -11,6 +11,8 @@ memory and the current stream.  The C entry points are documented in
     transition()  -> win_transition
     attn_fwd()    -> win_attn_fwd
     pack()        -> win_pack
+    lpt()         -> win_lpt
+    plan_a()      -> win_plan_a
 
 If the library has not been built the first call raises ``WinAttnError``;
 there is no fallback implementation.
@@ -23,8 +25,8 @@ import os
 from collections import OrderedDict
 from dataclasses import dataclass
 
-__all__ = ["WinAttnError", "Plan", "Packed", "plan", "plan_cached", "pack", "gather", "scatter", "transition",
-           "attn_fwd", "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
+__all__ = ["WinAttnError", "Plan", "Packed", "Assignment", "Redistribution", "plan", "plan_cached", "pack", "lpt",
+           "plan_a", "gather", "scatter", "transition", "attn_fwd", "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
 
 REGULAR = 0
 SHIFTED = 1
@@ -69,6 +71,10 @@ def load_library():
     lib.win_attn_fwd.restype = ctypes.c_int
     lib.win_pack.argtypes = [i32, vp, vp, vp, vp, i32, vp, vp, vp, ctypes.POINTER(i32)]
     lib.win_pack.restype = ctypes.c_int
+    lib.win_lpt.argtypes = [i32, vp, i32, vp, vp, vp, vp]
+    lib.win_lpt.restype = ctypes.c_int
+    lib.win_plan_a.argtypes = [i64, i32, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.win_plan_a.restype = ctypes.c_int
     lib.win_strerror.argtypes = [ctypes.c_int]
     lib.win_strerror.restype = ctypes.c_char_p
     lib.win_build_info.argtypes = []
@@ -212,6 +218,70 @@ def pack(plans, align=64, device=None) -> Packed:
     total = offsets[R]
     dev = torch.device("cpu") if device is None else torch.device(device)
     return Packed(list(offsets), total, cu_out.numel() - 1, mx.value, perm_out[:total].to(dev), cu_out.to(dev))
+
+
+@dataclass
+class Assignment:
+    """Windows of one layout on `ranks` ranks (see ``win_lpt``)."""
+    ranks: int
+    owner: object         # torch.int32 [N]: rank of each window
+    order: object         # torch.int32 [N]: windows grouped by rank, ascending inside a rank
+    rank_offsets: object  # torch.int32 [ranks + 1]
+    rank_tokens: object   # torch.int64 [ranks]
+
+    def windows_of(self, r):
+        return self.order[int(self.rank_offsets[r]):int(self.rank_offsets[r + 1])].tolist()
+
+
+def _host_i32(t):
+    import torch
+    return t.detach().to("cpu", torch.int32).contiguous()
+
+
+def lpt(plan_or_cu, ranks) -> Assignment:
+    """LPT assignment of a plan's windows (or of the windows of a host or
+    device ``cu_seqlens``) to ``ranks`` ranks; host tensors out."""
+    import torch
+    lib = load_library()
+    cu = _host_i32(plan_or_cu.cu_seqlens if isinstance(plan_or_cu, Plan) else torch.as_tensor(plan_or_cu))
+    N = cu.numel() - 1
+    owner = torch.empty(N, dtype=torch.int32)
+    order = torch.empty(N, dtype=torch.int32)
+    offs = torch.empty(ranks + 1, dtype=torch.int32)
+    toks = torch.empty(ranks, dtype=torch.int64)
+    _check(lib.win_lpt(N, _ptr(cu), int(ranks), _ptr(owner), _ptr(order), _ptr(offs), _ptr(toks)), "win_lpt")
+    return Assignment(int(ranks), owner, order, offs, toks)
+
+
+@dataclass
+class Redistribution:
+    """Plan A tables between two (plan, assignment) pairs (see
+    ``win_plan_a``); host tensors."""
+    counts: object        # torch.int64 [ranks, ranks]
+    send_rows: object     # torch.int32 [L]
+    recv_pos: object      # torch.int32 [L]
+    exchange_required: bool
+
+
+def plan_a(src: Plan, src_assignment: Assignment, dst: Plan, dst_assignment: Assignment) -> Redistribution:
+    import torch
+    lib = load_library()
+    P = src_assignment.ranks
+    if dst_assignment.ranks != P or src.num_tokens != dst.num_tokens:
+        raise WinAttnError(-1, "plan_a needs two layouts of one grid on the same number of ranks")
+    L = src.num_tokens
+    sp, sc, so, sr = (_host_i32(x) for x in (src.perm, src.cu_seqlens, src_assignment.order,
+                                             src_assignment.rank_offsets))
+    dp, dc, do, dr = (_host_i32(x) for x in (dst.perm, dst.cu_seqlens, dst_assignment.order,
+                                             dst_assignment.rank_offsets))
+    counts = torch.empty((P, P), dtype=torch.int64)
+    send = torch.empty(L, dtype=torch.int32)
+    recv = torch.empty(L, dtype=torch.int32)
+    ex = ctypes.c_int32()
+    _check(lib.win_plan_a(L, P, _ptr(sp), _ptr(sc), src.num_windows, _ptr(so), _ptr(sr), _ptr(dp), _ptr(dc),
+                          dst.num_windows, _ptr(do), _ptr(dr), _ptr(counts), _ptr(send), _ptr(recv),
+                          ctypes.byref(ex)), "win_plan_a")
+    return Redistribution(counts, send, recv, bool(ex.value))
 
 
 def _rows(x):

@@ -31,6 +31,7 @@ SOURCES = [
     # file validates arguments with isfinite)
     ("attn_fwd.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Xarch_device", "-fno-honor-nans"]),
     ("abi.cpp", ["-x", "hip"]),
+    ("sp_plan.cpp", []),
 ]
 
 
