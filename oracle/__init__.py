@@ -21,5 +21,7 @@ pack       several requests' plans packed into one varlen call with alignment
 sp_plan    the single-GPU tables of window-aligned sequence parallelism: LPT
            assignment and Plan A redistribution, with the exchange simulated
            on fake ranks (sections "Planner", "Plan A redistribution").
+rope       window-local 3D rotary position embedding of queries and keys
+           (section "Reference quirks reproduced on purpose").
 """
-from . import plan, permute, attention, pack, sp_plan  # noqa: F401
+from . import plan, permute, attention, pack, sp_plan, rope  # noqa: F401

@@ -295,6 +295,64 @@ def check_plan_a_invariants(plan_a_fn, z_src, z_dst):
     assert bool(ex) == any(counts[r][d] for r in range(P) for d in range(P) if r != d)
 
 
+# ---------------------------------------------------------------------- RoPE pins
+
+def check_rope_worked_example(rotate_fn):
+    """Hand-derived rotations of unit vectors (tests/golden/rope_worked_example.json):
+    ``rotate_fn(x, pos, rope_dim)`` rotates the last axis of fp64 ``x``."""
+    r = load_golden("rope_worked_example.json")["rotation"]
+    for cse in r["cases"]:
+        x = np.zeros(r["head_dim"])
+        x[cse["unit"]] = 1.0
+        y = rotate_fn(x, r["position"], r["rope_dim"])
+        for k, v in cse["expect"].items():
+            assert abs(y[int(k)] - v) < 1e-12, (cse["unit"], k, y[int(k)], v)
+        assert abs(np.linalg.norm(y) - 1.0) < 1e-12
+
+
+def check_rope_positions(positions_fn, oracle_plan):
+    """Hand-derived window-local positions on the 3x4 grid, both layouts:
+    ``positions_fn(plan, text_len)`` returns one (pt, ph, pw) per row."""
+    g = load_golden("rope_worked_example.json")["positions"]
+    for m, key in ((oracle_plan.REGULAR, "regular"), (oracle_plan.SHIFTED, "shifted")):
+        p = oracle_plan.plan(*g["grid"], *g["window_counts"], m)
+        assert [list(x) for x in positions_fn(p, g["text_len"])] == g[key]
+
+
+def check_rope_properties(rotate_fn, rope_dim, head_dim, seed=0):
+    """What makes it a rotary position embedding (Su et al.): a rotation
+    (pair norms kept, channels past the span untouched), rotations compose
+    (rotating by p then by r equals rotating by p + r), and the dot product of
+    a rotated query and key depends only on their position difference."""
+    rng = np.random.default_rng(seed)
+    span = 3 * (rope_dim // 3)
+    for _ in range(4):
+        q, k = rng.standard_normal(head_dim), rng.standard_normal(head_dim)
+        p1, p2, sh = rng.integers(0, 40, 3), rng.integers(0, 40, 3), rng.integers(0, 40, 3)
+        y = rotate_fn(q, p1, rope_dim)
+        assert np.allclose(y[span:], q[span:], rtol=0, atol=0)
+        pairs = lambda v: np.hypot(v[0:span:2], v[1:span:2])
+        assert np.allclose(pairs(y), pairs(q), rtol=1e-13, atol=1e-13)
+        assert np.allclose(rotate_fn(y, p2, rope_dim), rotate_fn(q, p1 + p2, rope_dim), rtol=1e-11, atol=1e-11)
+        d0 = rotate_fn(q, p1, rope_dim) @ rotate_fn(k, p2, rope_dim)
+        d1 = rotate_fn(q, p1 + sh, rope_dim) @ rotate_fn(k, p2 + sh, rope_dim)
+        assert abs(d0 - d1) < 1e-10 * (1 + abs(d0))
+
+
+def check_rope_window_restart(positions_fn, oracle_plan, text_len=3):
+    """Every window restarts at 0: each window's first row (its box corner)
+    sits at (text_len, 0, 0), and no axial index reaches the window extent."""
+    for grid in [(5, 9, 16, 2, 6, 6), (21, 45, 80, 4, 3, 3)]:
+        for m in (oracle_plan.REGULAR, oracle_plan.SHIFTED):
+            p = oracle_plan.plan(*grid, m)
+            pos = positions_fn(p, text_len)
+            for i, (t0, t1, h0, h1, w0, w1) in enumerate(p.boxes):
+                a, e = p.cu_seqlens[i], p.cu_seqlens[i + 1]
+                assert tuple(pos[a]) == (text_len, 0, 0)
+                for x in pos[a:e]:
+                    assert text_len <= x[0] < text_len + t1 - t0 and 0 <= x[1] < h1 - h0 and 0 <= x[2] < w1 - w0
+
+
 # --------------------------------------------------------------- attention pins
 
 def torch_sdpa_masked(qc, kc, vc, window_of_token, scale):

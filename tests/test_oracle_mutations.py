@@ -337,3 +337,68 @@ def test_lpt_mutant_is_caught(flag, monkeypatch):
 def test_plan_a_mutant_is_caught(monkeypatch):
     monkeypatch.setattr(osp, "plan_a", _plan_a_source_order)
     assert _sp_pins_fail(), "pins did not catch Plan A packed in source order"
+
+
+# ---------------------------------------------------------------------- RoPE
+
+import math as _math  # noqa: E402
+
+from oracle import rope as orope  # noqa: E402
+
+
+def _rope_pins_fail():
+    try:
+        pins.check_rope_worked_example(orope.rotate)
+        pins.check_rope_positions(orope.window_local_positions, oplan)
+        pins.check_rope_properties(orope.rotate, 12, 14)
+        pins.check_rope_window_restart(orope.window_local_positions, oplan)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def _rotate_variant(axis_order=(0, 1, 2), half_split=False, span_exponent=False):
+    def rotate(x, pos, rope_dim, base=orope.DEFAULT_BASE):
+        d = rope_dim // 3
+        y = np.array(x, dtype=np.float64, copy=True)
+        for blk, axis in enumerate(axis_order):
+            for i in range(d // 2):
+                ang = pos[axis] * base ** (-2.0 * i / (rope_dim if span_exponent else d))
+                c, s = _math.cos(ang), _math.sin(ang)
+                a, b = (blk * d + i, blk * d + i + d // 2) if half_split else (blk * d + 2 * i, blk * d + 2 * i + 1)
+                y[..., a] = x[..., a] * c - x[..., b] * s
+                y[..., b] = x[..., a] * s + x[..., b] * c
+        return y
+    return rotate
+
+
+def _positions_variant(text_on_h=False, global_pos=False):
+    def window_local_positions(plan, text_len):
+        H, W = plan.H, plan.W
+        out = []
+        for i, (t0, t1, h0, h1, w0, w1) in enumerate(plan.boxes):
+            for j in range(plan.cu_seqlens[i], plan.cu_seqlens[i + 1]):
+                t, rem = divmod(plan.perm[j], H * W)
+                h, w = divmod(rem, W)
+                if global_pos:
+                    t0 = h0 = w0 = 0
+                pt, ph = t - t0, h - h0
+                out.append((pt, ph + text_len, w - w0) if text_on_h else (pt + text_len, ph, w - w0))
+        return out
+    return window_local_positions
+
+
+def test_unmutated_rope_passes():
+    assert not _rope_pins_fail()
+
+
+@pytest.mark.parametrize("kw", [{"axis_order": (2, 1, 0)}, {"half_split": True}, {"span_exponent": True}])
+def test_rope_rotation_mutant_is_caught(kw, monkeypatch):
+    monkeypatch.setattr(orope, "rotate", _rotate_variant(**kw))
+    assert _rope_pins_fail(), f"pins did not catch rotation mutant {kw}"
+
+
+@pytest.mark.parametrize("kw", [{"text_on_h": True}, {"global_pos": True}])
+def test_rope_position_mutant_is_caught(kw, monkeypatch):
+    monkeypatch.setattr(orope, "window_local_positions", _positions_variant(**kw))
+    assert _rope_pins_fail(), f"pins did not catch position mutant {kw}"
