@@ -122,6 +122,33 @@ class Step:
         perm_launch(lambda: wa.scatter(self.o, pl.perm, out=self.out))
 
 
+def rope_gather_rate(st, torch, reps=20, text_len=58):
+    """The window-local RoPE gather of Q into the shifted layout (rotary span
+    126 of 128 channels), timed on its own beside the step: GB/s of its one
+    read and one write of every row."""
+    wa, w = st.wa, st.w
+    if w.head_dim != 128:
+        return None
+    p = st.plans["S"]
+    loc = wa.local_positions(p, device="cuda")
+    tab = wa.rope_table(p, text_len, 126, device="cuda")
+    dst = st.bufs[0][0]
+    for _ in range(3):
+        wa.gather_rope(st.q, p, loc, tab, 126, out=dst)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(st.stream)
+    for _ in range(reps):
+        wa.gather_rope(st.q, p, loc, tab, 126, out=dst)
+    b.record(st.stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    gbs = st.perm_bytes_data / (ms * 1e-3) / 1e9
+    return {"kernel": "rope_rows_kernel (gather, shifted layout, rotary span 126/128, text_len 58)",
+            "avg_launch_ms": round(ms, 4), "bytes_per_launch": st.perm_bytes_data, "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def measured_traffic(kernel_prefix, workload):
     """HBM bytes per launch (read + write) recorded in profiles/hbm_traffic.txt
     for a kernel, or None when there is no record for this workload or the
@@ -294,6 +321,9 @@ def main():
     log(f"[bench] permutes: {len(perm_ms) // args.steps}/step, mean {sum(perm_ms) / len(perm_ms) * 1e3:.1f} us, "
         f"{perm_gbs:.0f} GB/s")
     value = attn_flops_step / (ms_step * 1e-3) / 1e12
+    rope = rope_gather_rate(st, torch)
+    if rope:
+        log(f"[bench] rope gather (beside the step): {rope['avg_launch_ms'] * 1e3:.1f} us, {rope['achieved']:.0f} GB/s")
     attn_traffic = measured_traffic("attn_fwd_kernel", w.name)
     perm_traffic = measured_traffic("permute_rows_kernel<transition>", w.name)
     res = {
@@ -328,6 +358,7 @@ def main():
                              "kernel": "permute_rows_kernel (gather, transition, scatter)",
                              "avg_launch_ms": round(sum(perm_ms) / len(perm_ms), 4),
                              "bytes_per_launch": perm_bytes_launch},
+        "roofline_rope_permute": rope,
     }
     if not args.no_ceilings:
         ceil = practical_ceilings(torch, w)

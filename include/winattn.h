@@ -17,6 +17,9 @@
  *   - win_attn_fwd    sections "Motivation" and "SeedVR2 integration":
  *                     attention only inside each window, one packed
  *                     variable-length call over cu_seqlens segments.
+ *   - win_plan_local, section "Reference quirks reproduced on purpose":
+ *     win_rope_table, window-local 3D rotary position embedding of queries
+ *     win_permute_rope and keys, fused into the gather / transition.
  *   - win_lpt,        sections "Planner" and "Plan A redistribution": the
  *     win_plan_a      single-GPU tables of window-aligned sequence
  *                     parallelism (window assignment, exchange tables).
@@ -162,6 +165,59 @@ int win_transition(const void* src, void* dst, const int32_t* inv_src, const int
 int win_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                  int32_t num_windows, int32_t max_seqlen, int64_t L, int32_t batch, int32_t heads,
                  int32_t head_dim, float softmax_scale, void* stream);
+
+/*
+ * Window-local coordinates of a layout's rows (window page, section
+ * "Reference quirks reproduced on purpose": rotary positions are window-local
+ * and restart at 0 in every window).  Row j of the window order (canonical
+ * token perm[j] of win_plan) gets local[3j], local[3j+1], local[3j+2] = its
+ * t, h, w minus the first t, h, w of its window.  Geometry arguments and
+ * errors as in win_plan; local is [3 L] int32, host memory filled before
+ * return (on_device 0) or device memory filled by a kernel on `stream` (1).
+ */
+int win_plan_local(int32_t T, int32_t H, int32_t W, int32_t nt, int32_t nh, int32_t nw, int32_t method,
+                   int32_t* local, int32_t on_device, void* stream);
+
+/*
+ * (cos, sin) table of window-local 3D rotary position embedding (same
+ * section): the rotated span is 3 * (rope_dim / 3) channels, three blocks of
+ * d = rope_dim / 3 for the t, h and w axial indices; pair (2i, 2i+1) of a
+ * block turns by position * base^(-2i/d) (the rotation of Su et al.,
+ * RoFormer).  Rows of the table: t positions text_len .. text_len + wt - 1,
+ * then h positions 0 .. wh - 1, then w positions 0 .. ww - 1 (wt, wh, ww are a
+ * plan's window extents, win_plan_info); each row holds d / 2 pairs of floats
+ * (cos, sin), computed in double and rounded to float.
+ *   table: host, (wt + wh + ww) * (rope_dim / 3) floats.
+ * Errors: WIN_EINVAL (non-positive extents, negative text_len, base <= 1 or
+ * not finite, rope_dim < 6, table NULL), WIN_EUNSUPPORTED (rope_dim / 3 odd).
+ */
+int win_rope_table(int32_t wt, int32_t wh, int32_t ww, int32_t text_len, int32_t rope_dim, double base,
+                   float* table);
+
+/*
+ * Gather or transition of query / key rows into a window layout with the
+ * layout's window-local rotary embedding applied on the way (same section;
+ * one read and one write of every row, as win_permute):
+ *   gather     (perm_dst NULL):  row j = rope(src[b, idx[j]], local[j])
+ *   transition (perm_dst given): row j = rope(src[b, idx[perm_dst[j]]], local[j])
+ * where idx is the gather table of the destination layout (gather) or the
+ * source layout's inv (transition, idx = inv_src), and local is the
+ * destination layout's win_plan_local table.  src rows are not rotated: each
+ * layout rotates the same un-rotated rows with its own positions.
+ *   src, dst  device bf16 [batch, L, heads, head_dim], 16-byte aligned, no overlap.
+ *   idx, perm_dst, local  device int32 ([L], [L], [3 L]); entries are clamped
+ *             into range as in win_permute.
+ *   table     device floats in win_rope_table's layout for (wt, wh, ww),
+ *             8-byte aligned; local entries are clamped to those extents.
+ *   head_dim  64 or 128; rope_dim <= head_dim with rope_dim / 3 even.
+ * Channels past 3 * (rope_dim / 3) keep their bits.  Rotated pairs are
+ * computed in fp32 and rounded to bf16 (nearest even).
+ * Errors: WIN_EINVAL, WIN_EUNSUPPORTED (head_dim, rope_dim, alignment),
+ * WIN_EOVERFLOW, WIN_EDEVICE.
+ */
+int win_permute_rope(const void* src, void* dst, const int32_t* idx, const int32_t* perm_dst, const int32_t* local,
+                     const float* table, int32_t wt, int32_t wh, int32_t ww, int64_t L, int32_t batch,
+                     int32_t heads, int32_t head_dim, int32_t rope_dim, void* stream);
 
 /*
  * Packing of several requests' plans into one varlen call (page "vLLM-Omni

@@ -12,6 +12,9 @@ memory and the current stream.  The C entry points are documented in
     attn_fwd()    -> win_attn_fwd
     pack()        -> win_pack
     lpt()         -> win_lpt
+    local_positions() -> win_plan_local
+    rope_table()      -> win_rope_table
+    gather_rope(), transition_rope() -> win_permute_rope
     plan_a()      -> win_plan_a
 
 If the library has not been built the first call raises ``WinAttnError``;
@@ -26,7 +29,8 @@ from collections import OrderedDict
 from dataclasses import dataclass
 
 __all__ = ["WinAttnError", "Plan", "Packed", "Assignment", "Redistribution", "plan", "plan_cached", "pack", "lpt",
-           "plan_a", "gather", "scatter", "transition", "attn_fwd", "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
+           "plan_a", "local_positions", "rope_table", "gather_rope", "transition_rope", "gather", "scatter",
+           "transition", "attn_fwd", "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
 
 REGULAR = 0
 SHIFTED = 1
@@ -75,6 +79,12 @@ def load_library():
     lib.win_lpt.restype = ctypes.c_int
     lib.win_plan_a.argtypes = [i64, i32, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
     lib.win_plan_a.restype = ctypes.c_int
+    lib.win_plan_local.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, i32, vp]
+    lib.win_plan_local.restype = ctypes.c_int
+    lib.win_rope_table.argtypes = [i32, i32, i32, i32, i32, ctypes.c_double, vp]
+    lib.win_rope_table.restype = ctypes.c_int
+    lib.win_permute_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, i32, i32, vp]
+    lib.win_permute_rope.restype = ctypes.c_int
     lib.win_strerror.argtypes = [ctypes.c_int]
     lib.win_strerror.restype = ctypes.c_char_p
     lib.win_build_info.argtypes = []
@@ -137,6 +147,7 @@ class Plan:
     inv: object         # torch.int32 [L]
     cu_seqlens: object  # torch.int32 [N+1]
     boxes: object       # torch.int32 [N, 6]
+    counts: tuple = None  # (nt, nh, nw) it was built with
 
 
 def plan(T, H, W, nt, nh, nw, method=REGULAR, device=None) -> Plan:
@@ -159,7 +170,7 @@ def plan(T, H, W, nt, nh, nw, method=REGULAR, device=None) -> Plan:
     _check(lib.win_plan(T, H, W, nt, nh, nw, method, ctypes.byref(info), _ptr(perm), _ptr(inv), _ptr(cu),
                         _ptr(boxes), 1 if on_dev else 0, stream), "win_plan")
     return Plan(T, H, W, method, info.wt, info.wh, info.ww, (info.segs_t, info.segs_h, info.segs_w),
-                N, info.max_seqlen, L, perm, inv, cu, boxes)
+                N, info.max_seqlen, L, perm, inv, cu, boxes, (nt, nh, nw))
 
 
 _PLAN_CACHE: "OrderedDict[tuple, Plan]" = OrderedDict()
@@ -282,6 +293,69 @@ def plan_a(src: Plan, src_assignment: Assignment, dst: Plan, dst_assignment: Ass
                           dst.num_windows, _ptr(do), _ptr(dr), _ptr(counts), _ptr(send), _ptr(recv),
                           ctypes.byref(ex)), "win_plan_a")
     return Redistribution(counts, send, recv, bool(ex.value))
+
+
+def local_positions(p: Plan, device=None):
+    """Window-local (t, h, w) of every row of ``p``'s window order: int32
+    [L, 3], filled on the host (device None) or by a device kernel."""
+    import torch
+    lib = load_library()
+    dev = torch.device("cpu") if device is None else torch.device(device)
+    out = torch.empty((p.num_tokens, 3), dtype=torch.int32, device=dev)
+    on_dev = dev.type == "cuda"
+    _check(lib.win_plan_local(p.T, p.H, p.W, *_window_counts(p), p.method, _ptr(out), 1 if on_dev else 0,
+                              _stream(out) if on_dev else None), "win_plan_local")
+    return out
+
+
+def _window_counts(p: Plan):
+    if getattr(p, "counts", None) is None:
+        raise WinAttnError(-1, "this plan does not record its window counts; build it with plan()")
+    return p.counts
+
+
+def rope_table(p: Plan, text_len, rope_dim, base=10000.0, device=None):
+    """(cos, sin) table for ``p``'s window extents (see win_rope_table)."""
+    import torch
+    lib = load_library()
+    n = (p.wt + p.wh + p.ww) * (rope_dim // 3)
+    t = torch.empty(n, dtype=torch.float32)
+    _check(lib.win_rope_table(p.wt, p.wh, p.ww, int(text_len), int(rope_dim), float(base), _ptr(t)), "win_rope_table")
+    return t if device is None else t.to(device)
+
+
+def _permute_rope(src, idx, perm_dst, local, table, p: Plan, rope_dim, out):
+    import torch
+    lib = load_library()
+    _require_cuda("src", src, torch.bfloat16)
+    for name, t in (("idx", idx), ("local", local)):
+        _require_cuda(name, t, torch.int32)
+    if perm_dst is not None:
+        _require_cuda("perm_dst", perm_dst, torch.int32)
+    _require_cuda("table", table, torch.float32)
+    if src.dim() != 4:
+        raise WinAttnError(-1, "src must be [B, L, heads, head_dim]")
+    B, L, Hh, D = src.shape
+    if out is None:
+        out = torch.empty_like(src)
+    _require_cuda("out", out, torch.bfloat16)
+    if out.shape != src.shape:
+        raise WinAttnError(-1, "out must have the shape of src")
+    _check(lib.win_permute_rope(_ptr(src), _ptr(out), _ptr(idx), _ptr(perm_dst), _ptr(local), _ptr(table), p.wt,
+                                p.wh, p.ww, L, B, Hh, D, int(rope_dim), _stream(src)), "win_permute_rope")
+    return out
+
+
+def gather_rope(src, p: Plan, local, table, rope_dim, out=None):
+    """Canonical -> ``p``'s window order with ``p``'s window-local RoPE:
+    ``out[b, j] = rope(src[b, p.perm[j]], local[j])``."""
+    return _permute_rope(src, p.perm, None, local, table, p, rope_dim, out)
+
+
+def transition_rope(src, src_plan: Plan, dst_plan: Plan, local_dst, table, rope_dim, out=None):
+    """Un-rotated rows in ``src_plan``'s window order -> ``dst_plan``'s window
+    order with ``dst_plan``'s window-local RoPE."""
+    return _permute_rope(src, src_plan.inv, dst_plan.perm, local_dst, table, dst_plan, rope_dim, out)
 
 
 def _rows(x):

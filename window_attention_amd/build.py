@@ -26,6 +26,7 @@ SOURCES = [
     # the size formula's double arithmetic must not be contracted
     ("plan.hip", ["-ffp-contract=off"]),
     ("permute.hip", []),
+    ("rope.hip", []),
     # MFMA results in VGPRs (the softmax reads every score: no AGPR copies);
     # no NaN quieting before each max (device code only: the host side of the
     # file validates arguments with isfinite)

@@ -30,6 +30,16 @@ __global__ void fill_tokens_kernel(GridGeom g, int64_t L, int32_t* __restrict__ 
     if (inv) inv[c] = (int32_t)j;
 }
 
+__global__ void fill_local_kernel(GridGeom g, int64_t L, int32_t* __restrict__ local) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= L) return;
+    const int64_t j = window_position(g, c);
+    const LocalPos p = window_local(g, c);
+    local[3 * j] = p.t;
+    local[3 * j + 1] = p.h;
+    local[3 * j + 2] = p.w;
+}
+
 __global__ void fill_windows_kernel(GridGeom g, int32_t N, int64_t L, int32_t* __restrict__ cu,
                                     int32_t* __restrict__ boxes) {
     const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -191,4 +201,41 @@ extern "C" int win_pack(int32_t num_requests, const int64_t* num_tokens, const i
     offsets[num_requests] = o;
     *max_seqlen = (int32_t)longest;
     return WIN_OK;
+}
+
+// win_plan_local: window-local coordinates of every row of a layout's window
+// order (page "Window-Aligned Sequence Parallelism (SeedVR2)", section
+// "Reference quirks reproduced on purpose": rotary positions restart at 0 in
+// every window).  Row j holds canonical token perm[j]; local[3j .. 3j+2] are
+// its (t, h, w) minus its window's first (t, h, w).
+extern "C" int win_plan_local(int32_t T, int32_t H, int32_t W, int32_t nt, int32_t nh, int32_t nw, int32_t method,
+                              int32_t* local, int32_t on_device, void* stream) {
+    if (!local) return WIN_EINVAL;
+    win_plan_info info;
+    const int st = win_plan(T, H, W, nt, nh, nw, method, &info, nullptr, nullptr, nullptr, nullptr, 0, nullptr);
+    if (st != WIN_OK) return st;
+    if (on_device != 0 && on_device != 1) return WIN_EINVAL;
+    const bool shifted = method == WIN_METHOD_SHIFTED;
+    GridGeom g;
+    g.T = T;
+    g.H = H;
+    g.W = W;
+    g.t = make_axis(T, info.wt, shifted);
+    g.h = make_axis(H, info.wh, shifted);
+    g.w = make_axis(W, info.ww, shifted);
+    const int64_t L = info.num_tokens;
+    if (!on_device) {
+        for (int64_t c = 0; c < L; ++c) {
+            const int64_t j = window_position(g, c);
+            const LocalPos p = window_local(g, c);
+            local[3 * j] = p.t;
+            local[3 * j + 1] = p.h;
+            local[3 * j + 2] = p.w;
+        }
+        return WIN_OK;
+    }
+    constexpr int kThreads = 256;
+    const int64_t blocks = ceil_div(L, kThreads);
+    fill_local_kernel<<<dim3((uint32_t)blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(g, L, local);
+    return launch_status() == WIN_OK ? WIN_OK : WIN_EDEVICE;
 }

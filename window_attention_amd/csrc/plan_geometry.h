@@ -100,4 +100,21 @@ WIN_HD int64_t window_position(const GridGeom& g, int64_t c) {
     return window_offset(g, st, sh, sw) + ((t - ts) * hl + (h - hs)) * wl + (w - ws);
 }
 
+// Window-local coordinates of canonical token c: its (t, h, w) minus the first
+// coordinate of its window on each axis.
+struct LocalPos {
+    int32_t t, h, w;
+};
+
+WIN_HD LocalPos window_local(const GridGeom& g, int64_t c) {
+    const int32_t t = (int32_t)(c / ((int64_t)g.H * g.W));
+    const int32_t rem = (int32_t)(c - (int64_t)t * g.H * g.W);
+    const int32_t h = rem / g.W, w = rem - h * g.W;
+    LocalPos p;
+    p.t = t - axis_start(g.t, axis_seg(g.t, t));
+    p.h = h - axis_start(g.h, axis_seg(g.h, h));
+    p.w = w - axis_start(g.w, axis_seg(g.w, w));
+    return p;
+}
+
 }  // namespace winattn
