@@ -23,5 +23,8 @@ sp_plan    the single-GPU tables of window-aligned sequence parallelism: LPT
            on fake ranks (sections "Planner", "Plan A redistribution").
 rope       window-local 3D rotary position embedding of queries and keys
            (section "Reference quirks reproduced on purpose").
+text_attention
+           [video window, replicated text] segments and the text stream's
+           mean over windows (sections "SeedVR2 integration", "Text stream").
 """
-from . import plan, permute, attention, pack, sp_plan, rope  # noqa: F401
+from . import plan, permute, attention, pack, sp_plan, rope, text_attention  # noqa: F401

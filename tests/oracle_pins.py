@@ -353,6 +353,93 @@ def check_rope_window_restart(positions_fn, oracle_plan, text_len=3):
                     assert text_len <= x[0] < text_len + t1 - t0 and 0 <= x[1] < h1 - h0 and 0 <= x[2] < w1 - w0
 
 
+# ------------------------------------------------------------ text attention pins
+
+def check_text_closed_form(fn, seed=0):
+    """Uniform attention, from the page's two rules alone: with zero queries
+    every row of a segment attends uniformly, so a video row of window w gets
+    the mean of its segment's values, (n_w a_w + T b) / (n_w + T) when the
+    window's values are the constant a_w and the text values the constant b;
+    the text output is that same per-window mean averaged with equal weight per
+    window (not per token).  ``fn(q, k, v, cu, tq, tk, tv)`` returns (video,
+    text)."""
+    rng = np.random.default_rng(seed)
+    cu = [0, 1, 6, 6, 9]                      # windows of 1, 5, 0 and 3 tokens
+    B, Hh, D, T = 2, 3, 8, 4
+    L = cu[-1]
+    q = np.zeros((B, L, Hh, D))
+    k = rng.standard_normal((B, L, Hh, D))
+    tq = np.zeros((B, T, Hh, D))
+    tk = rng.standard_normal((B, T, Hh, D))
+    a = rng.standard_normal((B, len(cu) - 1, Hh))
+    bval = rng.standard_normal((B, Hh))
+    v = np.zeros((B, L, Hh, D))
+    for i in range(len(cu) - 1):
+        v[:, cu[i]:cu[i + 1]] = a[:, i][:, None, :, None]
+    tv = np.broadcast_to(bval[:, None, :, None], (B, T, Hh, D)).copy()
+    o, text = fn(q, k, v, cu, tq, tk, tv)[:2]
+    seg_mean = [(n * a[:, i] + T * bval) / (n + T) for i, n in enumerate(np.diff(cu))]
+    for i in range(len(cu) - 1):
+        for t in range(cu[i], cu[i + 1]):
+            assert np.allclose(o[:, t], seg_mean[i][:, :, None], rtol=0, atol=1e-12)
+    want_text = sum(seg_mean) / (len(cu) - 1)
+    assert np.allclose(text, np.broadcast_to(want_text[:, None, :, None], text.shape), rtol=0, atol=1e-12)
+
+
+def check_text_brute_force(fn, seed=1):
+    """Library routine: torch's scaled_dot_product_attention in float64 over
+    one sequence in which every window is followed by its own copy of the
+    text, with a same-segment mask; the text output is the mean over windows
+    of the copies' outputs."""
+    import torch
+    F = torch.nn.functional
+    rng = np.random.default_rng(seed)
+    cu = [0, 3, 7, 12]
+    B, Hh, D, T = 1, 2, 16, 5
+    L, N = cu[-1], len(cu) - 1
+    q, k, v = (rng.standard_normal((B, L, Hh, D)) for _ in range(3))
+    tq, tk, tv = (rng.standard_normal((B, T, Hh, D)) for _ in range(3))
+    seq = {x: [] for x in "qkv"}
+    seg = []
+    for i in range(N):
+        a, e = cu[i], cu[i + 1]
+        for name, src, txt in (("q", q, tq), ("k", k, tk), ("v", v, tv)):
+            seq[name].append(np.concatenate([src[:, a:e], txt], axis=1))
+        seg += [i] * (e - a + T)
+    Q, K, V = (torch.as_tensor(np.concatenate(seq[x], axis=1)).permute(0, 2, 1, 3).contiguous() for x in "qkv")
+    seg = torch.as_tensor(seg)
+    mask = seg[:, None] == seg[None, :]
+    out = F.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=1 / math.sqrt(D)).permute(0, 2, 1, 3).numpy()
+    o, text = fn(q, k, v, cu, tq, tk, tv)[:2]
+    pos, texts = 0, []
+    for i in range(N):
+        n = cu[i + 1] - cu[i]
+        assert np.allclose(o[:, cu[i]:cu[i + 1]], out[:, pos:pos + n], rtol=0, atol=1e-12)
+        texts.append(out[:, pos + n:pos + n + T])
+        pos += n + T
+    assert np.allclose(text, sum(texts) / N, rtol=0, atol=1e-12)
+
+
+def check_text_isolation(fn, seed=2):
+    """Changing one window's video rows leaves every other window's video
+    outputs unchanged, and moves the text output by exactly 1/N of that
+    window's text-output change."""
+    rng = np.random.default_rng(seed)
+    cu = [0, 4, 9, 11]
+    B, Hh, D, T = 1, 2, 8, 3
+    L, N = cu[-1], len(cu) - 1
+    q, k, v = (rng.standard_normal((B, L, Hh, D)) for _ in range(3))
+    tq, tk, tv = (rng.standard_normal((B, T, Hh, D)) for _ in range(3))
+    o1, t1, per1 = fn(q, k, v, cu, tq, tk, tv)
+    q2, k2, v2 = (x.copy() for x in (q, k, v))
+    for x in (q2, k2, v2):
+        x[:, 4:9] = rng.standard_normal((B, 5, Hh, D))
+    o2, t2, per2 = fn(q2, k2, v2, cu, tq, tk, tv)
+    assert np.array_equal(o1[:, :4], o2[:, :4]) and np.array_equal(o1[:, 9:], o2[:, 9:])
+    assert np.array_equal(per1[:, 0], per2[:, 0]) and np.array_equal(per1[:, 2], per2[:, 2])
+    assert np.allclose(t2 - t1, (per2[:, 1] - per1[:, 1]) / N, rtol=0, atol=1e-12)
+
+
 # --------------------------------------------------------------- attention pins
 
 def torch_sdpa_masked(qc, kc, vc, window_of_token, scale):

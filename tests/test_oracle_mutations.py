@@ -402,3 +402,59 @@ def test_rope_rotation_mutant_is_caught(kw, monkeypatch):
 def test_rope_position_mutant_is_caught(kw, monkeypatch):
     monkeypatch.setattr(orope, "window_local_positions", _positions_variant(**kw))
     assert _rope_pins_fail(), f"pins did not catch position mutant {kw}"
+
+
+# ------------------------------------------------------------ text attention
+
+from oracle import text_attention as otxt  # noqa: E402
+
+
+def _text_pins_fail():
+    try:
+        pins.check_text_closed_form(otxt.text_window_attention)
+        pins.check_text_brute_force(otxt.text_window_attention)
+        pins.check_text_isolation(otxt.text_window_attention)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def _text_variant(video_without_text=False, token_weighted=False, text_only_keys=False, count_plus_one=False):
+    def text_window_attention(q, k, v, cu, tq, tk, tv, scale=None):
+        B, L, Hh, D = q.shape
+        T = tq.shape[1]
+        s = 1.0 / math.sqrt(D) if scale is None else scale
+        N = len(cu) - 1
+        o = np.zeros((B, L, Hh, D))
+        per = np.zeros((B, N, T, Hh, D))
+        weights = []
+        for i in range(N):
+            a, e = cu[i], cu[i + 1]
+            weights.append(e - a)
+            for b in range(B):
+                for h in range(Hh):
+                    ks = np.concatenate([k[b, a:e, h], tk[b, :, h]])
+                    vs = np.concatenate([v[b, a:e, h], tv[b, :, h]])
+                    if e > a:
+                        kk, vv = (k[b, a:e, h], v[b, a:e, h]) if video_without_text else (ks, vs)
+                        o[b, a:e, h] = oatt.head_attention(q[b, a:e, h], kk, vv, s)[0]
+                    if T:
+                        kk, vv = (tk[b, :, h], tv[b, :, h]) if text_only_keys else (ks, vs)
+                        per[b, i, :, h] = oatt.head_attention(tq[b, :, h], kk, vv, s)[0]
+        if token_weighted:
+            w = np.asarray(weights, dtype=float) + T
+            text = np.einsum("bn...,n->b...", per, w) / w.sum()
+        else:
+            text = per.sum(axis=1) / (N + 1 if count_plus_one else N)
+        return o, text, per
+    return text_window_attention
+
+
+def test_unmutated_text_attention_passes():
+    assert not _text_pins_fail()
+
+
+@pytest.mark.parametrize("flag", ["video_without_text", "token_weighted", "text_only_keys", "count_plus_one"])
+def test_text_attention_mutant_is_caught(flag, monkeypatch):
+    monkeypatch.setattr(otxt, "text_window_attention", _text_variant(**{flag: True}))
+    assert _text_pins_fail(), f"pins did not catch text-attention mutant {flag}"
