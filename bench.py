@@ -149,6 +149,42 @@ def rope_gather_rate(st, torch, reps=20, text_len=58):
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def text_attention_rate(st, torch, text_len=256, reps=10):
+    """Window attention over [video window, replicated text] segments in the
+    shifted layout, timed on its own beside the step (the text stream is not
+    part of the step's schedule): useful TFLOP/s of the segment attention of
+    every window, the per-window text rows included, over the whole call (the
+    attention kernel and the text mean)."""
+    from window_attention_amd.inputs import normal
+    wa, w = st.wa, st.w
+    p = st.plans["S"]
+    tq, tk, tv = (normal((w.batch, text_len, w.heads, w.head_dim), 800 + t, w.sigma, device="cuda") for t in range(3))
+    N = p.num_windows
+    ws = torch.empty((w.batch, N, text_len, w.heads, w.head_dim), dtype=torch.float32, device="cuda")
+    o, to = torch.empty_like(st.q), torch.empty_like(tq)
+    src = st.bufs[0]
+    for x, dst in zip((st.q, st.k, st.v), src):
+        wa.gather(x, p.perm, out=dst)
+    for _ in range(3):
+        wa.attn_fwd_text(src[0], src[1], src[2], p.cu_seqlens, p.max_seqlen, tq, tk, tv, out=o, text_out=to,
+                         workspace=ws)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(st.stream)
+    for _ in range(reps):
+        wa.attn_fwd_text(src[0], src[1], src[2], p.cu_seqlens, p.max_seqlen, tq, tk, tv, out=o, text_out=to,
+                         workspace=ws)
+    b.record(st.stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    cu = p.cu_seqlens.cpu().tolist()
+    flops = sum(4 * (cu[i + 1] - cu[i] + text_len) ** 2 * w.head_dim for i in range(N)) * w.heads * w.batch
+    tfs = flops / (ms * 1e-3) / 1e12
+    return {"kernel": f"attn_fwd_kernel (text rows) + text_mean_kernel, shifted layout, {text_len} text rows",
+            "avg_call_ms": round(ms, 4), "flops_per_call": flops, "achieved": round(tfs, 2),
+            "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4)}
+
+
 def measured_traffic(kernel_prefix, workload):
     """HBM bytes per launch (read + write) recorded in profiles/hbm_traffic.txt
     for a kernel, or None when there is no record for this workload or the
@@ -324,6 +360,9 @@ def main():
     rope = rope_gather_rate(st, torch)
     if rope:
         log(f"[bench] rope gather (beside the step): {rope['avg_launch_ms'] * 1e3:.1f} us, {rope['achieved']:.0f} GB/s")
+    text = text_attention_rate(st, torch) if w.head_dim == 128 else None
+    if text:
+        log(f"[bench] text attention (beside the step): {text['avg_call_ms']:.3f} ms, {text['achieved']:.0f} TFLOP/s")
     attn_traffic = measured_traffic("attn_fwd_kernel", w.name)
     perm_traffic = measured_traffic("permute_rows_kernel<transition>", w.name)
     res = {
@@ -359,6 +398,7 @@ def main():
                              "avg_launch_ms": round(sum(perm_ms) / len(perm_ms), 4),
                              "bytes_per_launch": perm_bytes_launch},
         "roofline_rope_permute": rope,
+        "roofline_text_attention": text,
     }
     if not args.no_ceilings:
         ceil = practical_ceilings(torch, w)

@@ -17,6 +17,9 @@
  *   - win_attn_fwd    sections "Motivation" and "SeedVR2 integration":
  *                     attention only inside each window, one packed
  *                     variable-length call over cu_seqlens segments.
+ *   - win_attn_fwd_text  sections "SeedVR2 integration" and "Text stream":
+ *                     [video window, replicated text] segments and the text
+ *                     output averaged over windows.
  *   - win_plan_local, section "Reference quirks reproduced on purpose":
  *     win_rope_table, window-local 3D rotary position embedding of queries
  *     win_permute_rope and keys, fused into the gather / transition.
@@ -295,6 +298,36 @@ int win_plan_a(int64_t L, int32_t ranks, const int32_t* src_perm, const int32_t*
                const int32_t* dst_cu, int32_t dst_windows, const int32_t* dst_order,
                const int32_t* dst_rank_offsets, int64_t* counts, int32_t* send_rows, int32_t* recv_pos,
                int32_t* exchange_required);
+
+/*
+ * Text-augmented window attention (window page, sections "SeedVR2
+ * integration" and "Text stream"): every window's segment is its video rows
+ * followed by the text rows, replicated for each window.
+ *   video row of window i: softmax over [window i's keys, text keys] (scale
+ *     softmax_scale), written to o (and lse) as in win_attn_fwd;
+ *   text rows: once per window, softmax over the same segment; the normalized
+ *     per-window outputs go to text_partial (fp32), and text_o receives their
+ *     sum over the num_windows segments divided by num_windows (fp32 sum in
+ *     window order, rounded once to bf16).
+ * Arguments as in win_attn_fwd, plus
+ *   text_q, text_k, text_v  device bf16 [batch, text_len, heads, head_dim],
+ *                           16-byte aligned (shared by every window);
+ *   text_len >= 0           (0: exactly win_attn_fwd; the text pointers are
+ *                           then not used);
+ *   text_o                  device bf16 [batch, text_len, heads, head_dim] out;
+ *   text_partial            device fp32 workspace
+ *                           [batch, num_windows, text_len, heads, head_dim],
+ *                           16-byte aligned, owned by the caller, overwritten.
+ * Every segment counts as a window in the division, zero-length ones too
+ * (their text output attends to the text alone).  text_o and text_partial
+ * must not overlap any input or output.
+ * Errors: as win_attn_fwd; WIN_EINVAL also for text_len > 0 with a null text
+ * pointer or num_windows == 0.
+ */
+int win_attn_fwd_text(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+                      int32_t num_windows, int32_t max_seqlen, int64_t L, int32_t batch, int32_t heads,
+                      int32_t head_dim, float softmax_scale, const void* text_q, const void* text_k,
+                      const void* text_v, int32_t text_len, void* text_o, float* text_partial, void* stream);
 
 /* Static string naming a status code. */
 const char* win_strerror(int status);

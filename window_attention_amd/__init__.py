@@ -10,6 +10,7 @@ memory and the current stream.  The C entry points are documented in
     scatter()     -> win_permute(mode=WIN_SCATTER)
     transition()  -> win_transition
     attn_fwd()    -> win_attn_fwd
+    attn_fwd_text() -> win_attn_fwd_text
     pack()        -> win_pack
     lpt()         -> win_lpt
     local_positions() -> win_plan_local
@@ -30,7 +31,7 @@ from dataclasses import dataclass
 
 __all__ = ["WinAttnError", "Plan", "Packed", "Assignment", "Redistribution", "plan", "plan_cached", "pack", "lpt",
            "plan_a", "local_positions", "rope_table", "gather_rope", "transition_rope", "gather", "scatter",
-           "transition", "attn_fwd", "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
+           "transition", "attn_fwd", "attn_fwd_text", "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
 
 REGULAR = 0
 SHIFTED = 1
@@ -85,6 +86,9 @@ def load_library():
     lib.win_rope_table.restype = ctypes.c_int
     lib.win_permute_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, i32, i32, vp]
     lib.win_permute_rope.restype = ctypes.c_int
+    lib.win_attn_fwd_text.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, vp, vp, vp, i32,
+                                      vp, vp, vp]
+    lib.win_attn_fwd_text.restype = ctypes.c_int
     lib.win_strerror.argtypes = [ctypes.c_int]
     lib.win_strerror.restype = ctypes.c_char_p
     lib.win_build_info.argtypes = []
@@ -437,3 +441,43 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, out=None, retu
     _check(lib.win_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), N, int(max_seqlen),
                             L, B, Hh, D, float(softmax_scale), _stream(q)), "win_attn_fwd")
     return (out, lse) if return_lse else out
+
+
+def attn_fwd_text(q, k, v, cu_seqlens, max_seqlen, text_q, text_k, text_v, softmax_scale=None, out=None,
+                  text_out=None, workspace=None, return_lse=False):
+    """Window attention over [video window, replicated text] segments; returns
+    ``(out, text_out)`` (plus ``lse`` when asked).  ``workspace`` is the fp32
+    [B, num_windows, text_len, heads, head_dim] buffer of per-window text
+    outputs (allocated here when not given)."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require_cuda(name, t, torch.bfloat16)
+        if t.dim() != 4 or t.shape != q.shape:
+            raise WinAttnError(-1, f"{name} must be [B, L, heads, head_dim] like q")
+    B, L, Hh, D = q.shape
+    for name, t in (("text_q", text_q), ("text_k", text_k), ("text_v", text_v)):
+        _require_cuda(name, t, torch.bfloat16)
+        if t.dim() != 4 or t.shape != text_q.shape or t.shape[0] != B or t.shape[2:] != q.shape[2:]:
+            raise WinAttnError(-1, f"{name} must be [B, text_len, heads, head_dim] like text_q")
+    _require_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    T = text_q.shape[1]
+    N = cu_seqlens.numel() - 1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if text_out is None:
+        text_out = torch.empty_like(text_q)
+    if workspace is None:
+        workspace = torch.empty((B, max(N, 0), T, Hh, D), dtype=torch.float32, device=q.device)
+    _require_cuda("out", out, torch.bfloat16)
+    _require_cuda("text_out", text_out, torch.bfloat16)
+    _require_cuda("workspace", workspace, torch.float32)
+    if out.shape != q.shape or text_out.shape != text_q.shape or workspace.numel() < B * N * T * Hh * D:
+        raise WinAttnError(-1, "out, text_out or workspace has the wrong size")
+    lse = torch.empty((B, Hh, L), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.win_attn_fwd_text(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), N,
+                                 int(max_seqlen), L, B, Hh, D, float(softmax_scale), _ptr(text_q), _ptr(text_k),
+                                 _ptr(text_v), T, _ptr(text_out), _ptr(workspace), _stream(q)), "win_attn_fwd_text")
+    return (out, text_out, lse) if return_lse else (out, text_out)

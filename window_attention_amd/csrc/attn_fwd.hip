@@ -80,6 +80,13 @@ struct AttnParams {
     int32_t pairs;     // batch * num_windows * heads
     float scale;       // softmax scale
     float scale_log2;  // softmax scale * log2(e)
+    // text rows appended to every window's segment (none when text_len == 0)
+    const bf16* tq;    // [batch, text_len, heads, head_dim]
+    const bf16* tk;
+    const bf16* tv;
+    float* tpart;      // per-window text outputs [batch, num_windows, text_len, heads, head_dim]
+    int32_t text_len;
+    int32_t qtiles_v;  // video query tiles per (batch, window, head); the text's follow
 };
 
 template <int D>
@@ -194,6 +201,41 @@ struct TileJob {
         for (int i = 0; i < TC::kPerWave; ++i) issue(wave, i);
     }
 };
+
+// The keys of one (batch, window, head): the window's rows, then the text
+// rows (page "Window-Aligned Sequence Parallelism (SeedVR2)", section
+// "SeedVR2 integration": segments [video window, replicated text]).  Key
+// tile t holds window rows kBN t .. for t < tw, else text rows
+// kBN (t - tw) ..: every tile draws from one source, so the text starts on a
+// tile boundary and the window's last tile is masked past its end.
+struct KeyRange {
+    const bf16* kw;
+    const bf16* vw;
+    int32_t nw;  // window rows
+    const bf16* kt;
+    const bf16* vt;
+    int32_t nt;  // text rows
+    int32_t tw;  // window tiles
+    // TEXT false: no text rows (the plain call); the selection compiles away
+    template <bool TEXT>
+    __device__ int32_t tiles() const {
+        return TEXT ? tw + (nt + kBN - 1) / kBN : tw;
+    }
+    // keys of tile t inside its source (kBN or more: no mask)
+    template <bool TEXT>
+    __device__ int32_t limit(int32_t t) const {
+        return !TEXT || t < tw ? nw - t * kBN : nt - (t - tw) * kBN;
+    }
+};
+
+template <int D, int NW, bool IS_V, bool TEXT>
+__device__ __forceinline__ TileJob<D, NW, IS_V> tile_job(const KeyRange& kr, uint32_t off0, size_t row_stride,
+                                                         int32_t t, LDS_AS char* __restrict__ buf) {
+    if constexpr (!TEXT) return TileJob<D, NW, IS_V>(off0, IS_V ? kr.vw : kr.kw, row_stride, t * kBN, kr.nw, buf);
+    const bool win = t < kr.tw;
+    const bf16* base = IS_V ? (win ? kr.vw : kr.vt) : (win ? kr.kw : kr.kt);
+    return TileJob<D, NW, IS_V>(off0, base, row_stride, win ? t * kBN : (t - kr.tw) * kBN, win ? kr.nw : kr.nt, buf);
+}
 
 // Running state of one wave: QB blocks of 32 query rows, online softmax in
 // base 2.  Probabilities are exp2(c * s - c * m_ref) with c = softmax_scale *
@@ -434,12 +476,12 @@ __device__ __forceinline__ void value_slot(WaveState<D, QB>& st, const LDS_AS ch
 //   values:  O += V(j)^T P(j)^T            || row max (first DBLK slots),
 //                                             exp2 of S(j+1) (the rest)
 // plus the copies of K(j+2) and V(j+1) into the buffers read in step j-1.
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, bool TEXT>
 __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)[QB][kBN / 32],
                                               const LDS_AS char* __restrict__ k_next,
                                               const LDS_AS char* __restrict__ v_cur, LDS_AS char* __restrict__ k_fill,
-                                              LDS_AS char* __restrict__ v_fill, const bf16* kbase, const bf16* vbase,
-                                              size_t row_stride, int j, int n, float c, int wave, int lane) {
+                                              LDS_AS char* __restrict__ v_fill, const KeyRange& kr, size_t row_stride,
+                                              int j, float c, int wave, int lane) {
     constexpr int DBLK = WaveState<D, QB>::DBLK;
     constexpr int NV = DBLK * (kBN / 16);
     constexpr int NE = NV - DBLK;                    // exp slots
@@ -450,8 +492,8 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
     asm volatile("" : "+v"(st.koff0), "+v"(st.kcopy), "+v"(st.vcopy));
     const int h = lane >> 5;
     apply_pending_rescale(st);
-    const TileJob<D, NW, false> kjob(st.kcopy, kbase, row_stride, (j + 2) * kBN, n, k_fill);
-    const TileJob<D, NW, true> vjob(st.vcopy, vbase, row_stride, (j + 1) * kBN, n, v_fill);
+    const TileJob<D, NW, false> kjob = tile_job<D, NW, false, TEXT>(kr, st.kcopy, row_stride, j + 2, k_fill);
+    const TileJob<D, NW, true> vjob = tile_job<D, NW, true, TEXT>(kr, st.vcopy, row_stride, j + 1, v_fill);
     slot_fence();
     // scores stream
     PackedP pp[QB];
@@ -463,7 +505,7 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
     score_slots<D, NW, QB, true>(st, k_next, v_cur, s, vf, pf, pp, rs, kjob, vjob, wave);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += rs[qb];
-    const int lim = n - (j + 1) * kBN;
+    const int lim = kr.limit<TEXT>(j + 1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mask_tail(s[qb], lim, h);
     slot_fence();
@@ -527,12 +569,12 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
 
 // Step j of a wave with no query row inside the window: only its share of
 // the tile copies (the LDS tiles are shared by the workgroup).
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, bool TEXT>
 __device__ __forceinline__ void copy_step(const WaveState<D, QB>& st, LDS_AS char* __restrict__ k_fill,
-                                          LDS_AS char* __restrict__ v_fill, const bf16* kbase, const bf16* vbase,
-                                          size_t row_stride, int j, int n, int wave) {
-    TileJob<D, NW, false>(st.kcopy, kbase, row_stride, (j + 2) * kBN, n, k_fill).issue_all(wave);
-    TileJob<D, NW, true>(st.vcopy, vbase, row_stride, (j + 1) * kBN, n, v_fill).issue_all(wave);
+                                          LDS_AS char* __restrict__ v_fill, const KeyRange& kr, size_t row_stride,
+                                          int j, int wave) {
+    tile_job<D, NW, false, TEXT>(kr, st.kcopy, row_stride, j + 2, k_fill).issue_all(wave);
+    tile_job<D, NW, true, TEXT>(kr, st.vcopy, row_stride, j + 1, v_fill).issue_all(wave);
 }
 
 // P V product of the last tile, whose probabilities are in pf.
@@ -568,7 +610,7 @@ constexpr int waves_per_simd() {
     return QB == 1 ? 2 : 1;
 }
 
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, bool TEXT>
 __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel(AttnParams p) {
     using Ly = Layout<D>;
     using St = WaveState<D, QB>;
@@ -587,8 +629,12 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     const int xcd = bid & 7;
     const int slot = bid >> 3;
     const int pair = (slot / p.qtiles) * 8 + xcd;
-    const int qt = slot % p.qtiles;
+    const int qt_all = slot % p.qtiles;
     if (pair >= p.pairs) return;
+    // video query tiles first, then the text's (rows of the text appended to
+    // this window's segment)
+    const bool text_rows = TEXT && qt_all >= p.qtiles_v;
+    const int qt = text_rows ? qt_all - p.qtiles_v : qt_all;
     const int head = pair % p.heads;
     const int bw = pair / p.heads;
     const int win = bw % p.num_windows;
@@ -597,22 +643,31 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     start = start < 0 ? 0 : (start > p.L ? p.L : start);
     end = end < start ? start : (end > p.L ? p.L : end);
     const int n = end - start;
+    const int nq = text_rows ? p.text_len : n;  // query rows of this work item
     const int q0 = qt * BM;
-    if (q0 >= n) return;
+    if (q0 >= nq) return;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5;
     const size_t row_stride = (size_t)p.heads * D;
     const size_t base_off = ((size_t)b * p.L + start) * row_stride + (size_t)head * D;
-    const bf16* kbase = p.k + base_off;
-    const bf16* vbase = p.v + base_off;
+    const size_t text_off = (size_t)b * p.text_len * row_stride + (size_t)head * D;
+    KeyRange kr;
+    kr.kw = p.k + base_off;
+    kr.vw = p.v + base_off;
+    kr.nw = n;
+    kr.kt = p.text_len ? p.tk + text_off : kr.kw;
+    kr.vt = p.text_len ? p.tv + text_off : kr.vw;
+    kr.nt = p.text_len;
+    kr.tw = (n + kBN - 1) / kBN;
+    const bf16* qsrc = text_rows ? p.tq + text_off : p.q + base_off;
     const float c = p.scale_log2;
 
     St st;
     st.kcopy = TileCopy<D, NW, false>::src_off0(row_stride, wave, lane);
     st.vcopy = TileCopy<D, NW, true>::src_off0(row_stride, wave, lane);
-    const int nkv = (n + kBN - 1) / kBN;
+    const int nkv = kr.tiles<TEXT>();
     // V rows past the window end are never loaded: the V buffers start as
     // zeros (each wave clears the segments its own copies write, and waits for
     // that before they are issued)
@@ -626,16 +681,16 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     }
-    TileJob<D, NW, false>(st.kcopy, kbase, row_stride, 0, n, k0).issue_all(wave);
-    TileJob<D, NW, true>(st.vcopy, vbase, row_stride, 0, n, v0).issue_all(wave);
+    tile_job<D, NW, false, TEXT>(kr, st.kcopy, row_stride, 0, k0).issue_all(wave);
+    tile_job<D, NW, true, TEXT>(kr, st.vcopy, row_stride, 0, v0).issue_all(wave);
 
     // query row of this lane in block qb: q0 + (wave * QB + qb) * 32 + lane % 32
     const int qrow0 = q0 + wave * 32 * QB + (lane & 31);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qr = qrow0 + qb * 32;
-        const int qr_c = qr < n ? qr : n - 1;
-        const bf16x8* qp = reinterpret_cast<const bf16x8*>(p.q + base_off + (size_t)qr_c * row_stride);
+        const int qr_c = qr < nq ? qr : nq - 1;
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(qsrc + (size_t)qr_c * row_stride);
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) st.qf[qb][t] = qp[2 * t + h];
     }
@@ -674,23 +729,23 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     // ---- prologue: tile 0 scores and probabilities ---------------------------
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile 0 have landed
     __syncthreads();                      // ... and every wave's
-    TileJob<D, NW, false>(st.kcopy, kbase, row_stride, kBN, n, k1).issue_all(wave);
+    tile_job<D, NW, false, TEXT>(kr, st.kcopy, row_stride, 1, k1).issue_all(wave);
     // A wave whose query rows all lie past the window end (the last query
     // tile of a window) computes nothing; it still copies its share of every
     // tile and meets every barrier.
-    const bool active = q0 + wave * 32 * QB < n;
+    const bool active = q0 + wave * 32 * QB < nq;
     f32x16 pf[QB][kBN / 32];
     if (active) {
         bf16x8 vf_unused[DBLK * (kBN / 16)];
         PackedP pp_unused[QB];
         float rs_unused[QB];
-        const TileJob<D, NW, false> kj_unused(st.kcopy, kbase, row_stride, 0, 0, k1);
-        const TileJob<D, NW, true> vj_unused(st.vcopy, vbase, row_stride, 0, 0, v1);
+        const TileJob<D, NW, false> kj_unused(st.kcopy, kr.kw, row_stride, 0, 0, k1);
+        const TileJob<D, NW, true> vj_unused(st.vcopy, kr.vw, row_stride, 0, 0, v1);
         score_slots<D, NW, QB, false>(st, k0, k0, pf, vf_unused, pf, pp_unused, rs_unused, kj_unused, vj_unused,
                                       wave);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            mask_tail(pf[qb], n, h);
+            mask_tail(pf[qb], kr.limit<TEXT>(0), h);
             move_reference(st, qb, tile_max(pf[qb]), true, c);  // first reference: the tile max (O is still zero)
             tile_exp(pf[qb], c, st.mc[qb]);
         }
@@ -705,23 +760,23 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (active)
-            pipeline_step<D, NW, QB>(st, pf, k1, v0, k0, v1, kbase, vbase, row_stride, j, n, c, wave, lane);
+            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, c, wave, lane);
         else
-            copy_step<D, NW, QB>(st, k0, v1, kbase, vbase, row_stride, j, n, wave);
+            copy_step<D, NW, QB, TEXT>(st, k0, v1, kr, row_stride, j, wave);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (active)
-            pipeline_step<D, NW, QB>(st, pf, k0, v1, k1, v0, kbase, vbase, row_stride, j + 1, n, c, wave, lane);
+            pipeline_step<D, NW, QB, TEXT>(st, pf, k0, v1, k1, v0, kr, row_stride, j + 1, c, wave, lane);
         else
-            copy_step<D, NW, QB>(st, k1, v0, kbase, vbase, row_stride, j + 1, n, wave);
+            copy_step<D, NW, QB, TEXT>(st, k1, v0, kr, row_stride, j + 1, wave);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (j + 1 < nkv) {  // one more full step (tiles j, j+1), then the P V of tile j+1
         if (active)
-            pipeline_step<D, NW, QB>(st, pf, k1, v0, k0, v1, kbase, vbase, row_stride, j, n, c, wave, lane);
+            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, c, wave, lane);
         else
-            copy_step<D, NW, QB>(st, k0, v1, kbase, vbase, row_stride, j, n, wave);
+            copy_step<D, NW, QB, TEXT>(st, k0, v1, kr, row_stride, j, wave);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (active) final_pv(st, pf, v1);
@@ -736,7 +791,20 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
         const int qr = qrow0 + qb * 32;
         const float l_tot = pair_sum(st.l_run[qb]);
         const float inv = 1.f / l_tot;
-        if (qr < n) {
+        if (text_rows && qr < nq) {
+            // this window's text output, normalized, kept in fp32 for the mean
+            // over windows
+            float* trow = p.tpart + (((size_t)b * p.num_windows + win) * p.text_len + qr) * row_stride + head * D;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    f32x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = st.oacc[qb][db][4 * a + i] * inv;
+                    *reinterpret_cast<f32x4*>(trow + db * 32 + 8 * a + 4 * h) = x;
+                }
+        } else if (qr < nq) {
             bf16* orow = p.o + base_off + (size_t)qr * row_stride;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db)
@@ -756,16 +824,37 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     }
 }
 
+// Text stream of the window page (section "Text stream"): the text passed
+// on is the sum of the per-window text outputs over the window count,
+// summed in window order in fp32 and rounded once to bf16.  Thread i owns
+// four consecutive elements of one batch's text rows.
+__global__ __launch_bounds__(256) void text_mean_kernel(const float* __restrict__ part, bf16* __restrict__ out,
+                                                        int32_t num_windows, int64_t per_batch, int64_t total) {
+    const int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (e >= total) return;
+    const int64_t b = e / per_batch, r = e - b * per_batch;
+    const float* src = part + (size_t)b * num_windows * per_batch + r;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int32_t i = 0; i < num_windows; ++i) acc += *reinterpret_cast<const f32x4*>(src + (size_t)i * per_batch);
+    const float w = (float)num_windows;
+    const f32x4 m = {acc[0] / w, acc[1] / w, acc[2] / w, acc[3] / w};
+    *reinterpret_cast<bf16x4*>(out + e) = __builtin_convertvector(m, bf16x4);
+}
+
 template <int D, int NW, int QB>
 int launch_attn(const AttnParams& prm, int32_t max_seqlen, hipStream_t stream) {
     constexpr int BM = 32 * QB * NW;
     AttnParams p = prm;
-    p.qtiles = (max_seqlen + BM - 1) / BM;
+    p.qtiles_v = (max_seqlen + BM - 1) / BM;
+    p.qtiles = p.qtiles_v + (p.text_len + BM - 1) / BM;
     if (p.qtiles == 0 || p.pairs == 0) return WIN_OK;
     const int64_t groups = ((int64_t)p.pairs + 7) / 8;
     const int64_t blocks = groups * 8 * p.qtiles;
     if (blocks >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
-    attn_fwd_kernel<D, NW, QB><<<dim3((uint32_t)blocks), dim3(NW * 64), 0, stream>>>(p);
+    if (p.text_len > 0)
+        attn_fwd_kernel<D, NW, QB, true><<<dim3((uint32_t)blocks), dim3(NW * 64), 0, stream>>>(p);
+    else
+        attn_fwd_kernel<D, NW, QB, false><<<dim3((uint32_t)blocks), dim3(NW * 64), 0, stream>>>(p);
     return launch_status();
 }
 
@@ -782,11 +871,14 @@ int launch_attn(const AttnParams& prm, int32_t max_seqlen, hipStream_t stream) {
 
 using namespace winattn;
 
-extern "C" int win_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                            const int32_t* cu_seqlens, int32_t num_windows, int32_t max_seqlen, int64_t L,
-                            int32_t batch, int32_t heads, int32_t head_dim, float softmax_scale, void* stream) {
+namespace {
+
+int attn_impl(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+              int32_t num_windows, int32_t max_seqlen, int64_t L, int32_t batch, int32_t heads, int32_t head_dim,
+              float softmax_scale, const void* tq, const void* tk, const void* tv, int32_t text_len, void* text_o,
+              float* text_partial, void* stream) {
     if (!q || !k || !v || !o || !cu_seqlens) return WIN_EINVAL;
-    if (num_windows < 0 || max_seqlen < 0 || L < 0 || batch <= 0 || heads <= 0) return WIN_EINVAL;
+    if (num_windows < 0 || max_seqlen < 0 || L < 0 || batch <= 0 || heads <= 0 || text_len < 0) return WIN_EINVAL;
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return WIN_EINVAL;
     if (head_dim != 64 && head_dim != 128) return WIN_EUNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return WIN_EUNSUPPORTED;
@@ -801,7 +893,25 @@ extern "C" int win_attn_fwd(const void* q, const void* k, const void* v, void* o
     if (pairs >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
     // a key tile's rows are addressed with 32-bit buffer offsets
     if ((int64_t)kBN * heads * head_dim * 2 >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
-    if (num_windows == 0 || L == 0 || max_seqlen == 0) return WIN_OK;
+    const int64_t t_elems = (int64_t)batch * text_len * heads * head_dim;
+    const int64_t p_elems = t_elems * num_windows;
+    if (text_len > 0) {
+        if (!tq || !tk || !tv || !text_o || !text_partial || num_windows == 0) return WIN_EINVAL;
+        if (!aligned16(tq) || !aligned16(tk) || !aligned16(tv) || !aligned16(text_o) || !aligned16(text_partial))
+            return WIN_EUNSUPPORTED;
+        if (text_len >= ((int64_t)1 << 31) / 64 || p_elems >= ((int64_t)1 << 40)) return WIN_EOVERFLOW;
+        const uint64_t tb = (uint64_t)t_elems * 2, pb = (uint64_t)p_elems * 4;
+        const void* ins[6] = {q, k, v, tq, tk, tv};
+        for (const void* x : ins) {
+            const uint64_t xb = (x == q || x == k || x == v) ? bytes : tb;
+            if (overlaps(text_o, tb, x, xb) || overlaps(text_partial, pb, x, xb)) return WIN_EINVAL;
+        }
+        if (overlaps(text_o, tb, o, bytes) || overlaps(text_partial, pb, o, bytes) ||
+            overlaps(text_partial, pb, text_o, tb) || (lse && overlaps(lse, (uint64_t)batch * heads * L * 4,
+                                                                        text_partial, pb)))
+            return WIN_EINVAL;
+    }
+    if (num_windows == 0 || (text_len == 0 && (L == 0 || max_seqlen == 0))) return WIN_OK;
 
     AttnParams p;
     p.q = static_cast<const bf16*>(q);
@@ -817,7 +927,37 @@ extern "C" int win_attn_fwd(const void* q, const void* k, const void* v, void* o
     p.pairs = (int32_t)pairs;
     p.scale = softmax_scale;
     p.scale_log2 = softmax_scale * kLog2e;
+    p.tq = static_cast<const bf16*>(tq);
+    p.tk = static_cast<const bf16*>(tk);
+    p.tv = static_cast<const bf16*>(tv);
+    p.tpart = text_partial;
+    p.text_len = text_len;
+    p.qtiles_v = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (head_dim == 128) return launch_attn<128, WINATTN_NW, WINATTN_QB>(p, max_seqlen, s);
-    return launch_attn<64, WINATTN_NW, WINATTN_QB>(p, max_seqlen, s);
+    const int st = head_dim == 128 ? launch_attn<128, WINATTN_NW, WINATTN_QB>(p, max_seqlen, s)
+                                   : launch_attn<64, WINATTN_NW, WINATTN_QB>(p, max_seqlen, s);
+    if (st != WIN_OK || text_len == 0) return st;
+    const int64_t per_batch = (int64_t)text_len * heads * head_dim;
+    const int64_t threads = t_elems / 4;
+    text_mean_kernel<<<dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, s>>>(
+        text_partial, static_cast<bf16*>(text_o), num_windows, per_batch, t_elems);
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" int win_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens, int32_t num_windows, int32_t max_seqlen, int64_t L,
+                            int32_t batch, int32_t heads, int32_t head_dim, float softmax_scale, void* stream) {
+    return attn_impl(q, k, v, o, lse, cu_seqlens, num_windows, max_seqlen, L, batch, heads, head_dim, softmax_scale,
+                     nullptr, nullptr, nullptr, 0, nullptr, nullptr, stream);
+}
+
+extern "C" int win_attn_fwd_text(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int32_t* cu_seqlens, int32_t num_windows, int32_t max_seqlen, int64_t L,
+                                 int32_t batch, int32_t heads, int32_t head_dim, float softmax_scale,
+                                 const void* text_q, const void* text_k, const void* text_v, int32_t text_len,
+                                 void* text_o, float* text_partial, void* stream) {
+    return attn_impl(q, k, v, o, lse, cu_seqlens, num_windows, max_seqlen, L, batch, heads, head_dim, softmax_scale,
+                     text_q, text_k, text_v, text_len, text_o, text_partial, stream);
 }
