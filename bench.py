@@ -361,9 +361,16 @@ def main():
     if rope:
         log(f"[bench] rope gather (beside the step): {rope['avg_launch_ms'] * 1e3:.1f} us, {rope['achieved']:.0f} GB/s")
     text = text_attention_rate(st, torch) if w.head_dim == 128 else None
+    if rope:
+        t = measured_traffic("rope_rows_kernel", w.name)
+        rope["traffic"], rope["traffic_detail"] = (t["total_bytes"] if t else None), t
     if text:
+        t = measured_traffic("attn_fwd_kernel<128,4,1,true>", w.name)
+        m = measured_traffic("text_mean_kernel", w.name)
+        text["traffic"] = t["total_bytes"] + m["total_bytes"] if t and m else None
+        text["traffic_detail"] = {"attn_fwd_kernel": t, "text_mean_kernel": m} if t and m else None
         log(f"[bench] text attention (beside the step): {text['avg_call_ms']:.3f} ms, {text['achieved']:.0f} TFLOP/s")
-    attn_traffic = measured_traffic("attn_fwd_kernel", w.name)
+    attn_traffic = measured_traffic("attn_fwd_kernel<128,4,1,false>", w.name)
     perm_traffic = measured_traffic("permute_rows_kernel<transition>", w.name)
     res = {
         "metric": "window-attn useful TFLOP/s + permute GB/s, 21x45x80 grid bf16, 1 GPU",
