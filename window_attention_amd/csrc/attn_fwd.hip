@@ -13,6 +13,10 @@
 //     v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator layout a lane holds
 //     16 keys of ONE query column (lane % 32), so the softmax row max and row
 //     sum are in-lane reductions plus one exchange with lane ^ 32.
+//   * The softmax runs in base 2 on scores relative to a per-row reference
+//     m: Q is loaded as bf16(q * scale * log2 e), and every score chain
+//     starts from the accumulator value -m, so the MFMAs produce
+//     scale * log2(e) * q.k - m directly and a probability costs one exp2.
 //   * O^T = V^T P^T with the same instruction.  P^T is used straight from the
 //     score registers as the B operand: the 8 keys a lane supplies for a
 //     16-key step are the ones its accumulator already holds (keys
@@ -29,7 +33,10 @@
 //     16 lanes) are spread over the LDS banks.
 //   * The key loop is software pipelined: while the MFMAs of tile j+1's
 //     scores run, the VALU packs tile j's probabilities; while the MFMAs of
-//     tile j's P V product run, the VALU does tile j+1's row max and exp2.
+//     tile j's P V product run, the VALU does tile j+1's exp2 and row sums.
+//     No row max is taken on the common path: a tile's probabilities are
+//     bounded by its row sum, and only a sum above 2^kRescaleLog2 sends the
+//     tile down the rare path that moves the reference.
 //     The loop is laid out by hand in slots of one MFMA each, with the LDS
 //     reads of an operand issued a few MFMAs before its use and scheduling
 //     fences between slots, so that an MFMA never waits for a read issued
@@ -62,9 +69,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kBN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Rescaling is deferred until a tile's max exceeds the reference max by this
-// many powers of two, so probabilities stay below 2^kRescaleLog2.
-constexpr float kRescaleLog2 = 8.f;
+// The reference of a row moves (and O is rescaled) only when some lane's
+// probabilities of one tile sum to more than 2^kRescaleLog2; every
+// probability is then at most 2^kRescaleLog2.
+constexpr float kSumLimit = 256.f;  // 2^kRescaleLog2, kRescaleLog2 = 8
 
 struct AttnParams {
     const bf16* q;
@@ -155,10 +163,10 @@ struct TileCopy {
     }
     // segment i of this wave: per-lane offsets fixed for the whole loop,
     // segment i a uniform kRowsPerSeg rows further
-    __device__ static void segment(__amdgpu_buffer_rsrc_t src, uint32_t off0, uint32_t seg_bytes,
+    __device__ static void segment(__amdgpu_buffer_rsrc_t src, uint32_t off, uint32_t seg_bytes,
                                    LDS_AS char* __restrict__ tile, int wave, int i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (LDS_AS void*)(tile + (wave * kPerWave + i) * 1024), 16,
-                                                 off0 ^ chunk_xor(i), i * seg_bytes, 0, 0);
+                                                 off, i * seg_bytes, 0, 0);
     }
 };
 
@@ -177,15 +185,15 @@ template <int D, int NW, bool IS_V>
 struct TileJob {
     using TC = TileCopy<D, NW, IS_V>;
     __amdgpu_buffer_rsrc_t src;
-    uint32_t off0;       // per-lane source offset of segment 0
-    uint32_t seg_bytes;  // source bytes between consecutive segments of a lane
+    const uint32_t* offs;  // per-lane source offsets of the segments
+    uint32_t seg_bytes;    // source bytes between consecutive segments of a lane
     LDS_AS char* tile;
 
-    __device__ TileJob(uint32_t off0_, const bf16* base, size_t row_stride, int kv, int n, LDS_AS char* tile_)
-        : off0(off0_), tile(tile_) {
+    __device__ TileJob(const uint32_t* offs_, const bf16* base, size_t row_stride, int kv, int n, LDS_AS char* tile_)
+        : offs(offs_), tile(tile_) {
         const uint32_t row_bytes = (uint32_t)row_stride * 2;
-        int rows = n - kv;
-        rows = rows < 0 ? 0 : (rows > kBN ? kBN : rows);
+        // (a select and a min, not a clamp: the clamp becomes a vector med3)
+        const int rows = kv >= n ? 0 : (n - kv < kBN ? n - kv : kBN);
         seg_bytes = TC::Ly::kRowsPerSeg * row_bytes;
         // every input is wave-uniform; saying so keeps the resource in SGPRs
         // (the compiler would otherwise wrap each load in a readfirstlane loop)
@@ -195,7 +203,7 @@ struct TileJob {
         src = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(a_u), 0,
                                                 __builtin_amdgcn_readfirstlane(rows * (int)row_bytes), kBufferWord3);
     }
-    __device__ void issue(int wave, int i) const { TC::segment(src, off0, seg_bytes, tile, wave, i); }
+    __device__ void issue(int wave, int i) const { TC::segment(src, offs[i], seg_bytes, tile, wave, i); }
     __device__ void issue_all(int wave) const {
 #pragma unroll
         for (int i = 0; i < TC::kPerWave; ++i) issue(wave, i);
@@ -229,7 +237,7 @@ struct KeyRange {
 };
 
 template <int D, int NW, bool IS_V, bool TEXT>
-__device__ __forceinline__ TileJob<D, NW, IS_V> tile_job(const KeyRange& kr, uint32_t off0, size_t row_stride,
+__device__ __forceinline__ TileJob<D, NW, IS_V> tile_job(const KeyRange& kr, const uint32_t* off0, size_t row_stride,
                                                          int32_t t, LDS_AS char* __restrict__ buf) {
     if constexpr (!TEXT) return TileJob<D, NW, IS_V>(off0, IS_V ? kr.vw : kr.kw, row_stride, t * kBN, kr.nw, buf);
     const bool win = t < kr.tw;
@@ -238,23 +246,26 @@ __device__ __forceinline__ TileJob<D, NW, IS_V> tile_job(const KeyRange& kr, uin
 }
 
 // Running state of one wave: QB blocks of 32 query rows, online softmax in
-// base 2.  Probabilities are exp2(c * s - c * m_ref) with c = softmax_scale *
-// log2(e) and m_ref a reference max of the raw scores s.
+// base 2.  With c = softmax_scale * log2(e), the score of query q and key k
+// is x = c q.k (Q enters as bf16(c q)) and its probability exp2(x - mc), mc
+// a reference that no tile's probabilities exceed by much (see kSumLimit).
 template <int D, int QB>
 struct WaveState {
     static constexpr int KSTEPS = D / 16;
     static constexpr int DBLK = D / 32;
     bf16x8 qf[QB][KSTEPS];  // Q fragments, B operands of S^T = K Q^T
     f32x16 oacc[QB][DBLK];  // O^T accumulators: column = this lane's query
-    float m_ref[QB];        // reference max of the raw scores (equal in lanes l and l ^ 32)
-    float mc[QB];           // c * m_ref
-    float l_run[QB];        // sum of the bf16 probabilities this lane contributed
+    float mc[QB];           // reference of the scores x (equal in lanes l and l ^ 32)
+    f32x16 negm[QB];        // -mc in every accumulator register: the score chains start from it
+    float l_run[QB];        // sum of the fp32 probabilities this lane contributed
     float alpha[QB];        // O rescale factor owed since the reference last moved
     bool pending;           // wave-uniform: alpha must be applied before the next P V
     int koff0;              // LDS byte offset of the K operand at k step 0 (step t: ^ 32 t)
     int voff[DBLK];         // LDS byte offsets of the transposed V reads per O^T block
-    uint32_t kcopy;         // source offset of this lane's first K tile segment
-    uint32_t vcopy;         // source offset of this lane's first V tile segment
+    // source offsets of this lane's K and V tile segments (the first
+    // TileCopy::kPerWave entries are used)
+    uint32_t kcopy[Layout<D>::kSegs];
+    uint32_t vcopy[Layout<D>::kSegs];
 };
 
 // K fragment (A operand of S^T) number i of a key tile: fragments alternate
@@ -308,42 +319,50 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[kBN / 32]) {
     return pair_max(fmaxf(mx0, mx1));
 }
 
-// Move the reference max of growing lanes of query block qb to the tile max
-// and rebase the running sum.  Returns the factor O must be multiplied by once
-// every earlier P V product is in it (1 for lanes whose reference did not
-// move).
+// Move the reference of query block qb up by delta (0 in lanes whose
+// reference stays), rebasing the running sum and the value the score chains
+// start from.  Returns the factor O must be multiplied by once every earlier
+// P V product is in it.
 template <int D, int QB>
-__device__ __forceinline__ float move_reference(WaveState<D, QB>& st, int qb, float mx, bool grow, float c) {
-    const float m_new = grow ? mx : st.m_ref[qb];
-    const float alpha = __builtin_amdgcn_exp2f((st.m_ref[qb] - m_new) * c);
-    st.m_ref[qb] = m_new;
-    st.mc[qb] = m_new * c;
+__device__ __forceinline__ float move_reference(WaveState<D, QB>& st, int qb, float delta) {
+    const float alpha = __builtin_amdgcn_exp2f(-delta);
+    st.mc[qb] += delta;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.negm[qb][r] = -st.mc[qb];
     st.l_run[qb] *= alpha;
     return alpha;
 }
 
-// exp2 of one query block's scores against its reference, in place (fp32
-// probabilities, at most 2^kRescaleLog2).
-__device__ __forceinline__ void tile_exp(f32x16 (&s)[kBN / 32], float c, float mc) {
+// Sum of one query block's probabilities of a tile, in this lane.
+__device__ __forceinline__ float tile_sum(const f32x16 (&s)[kBN / 32]) {
+    float a = 0.f;
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mc));
+        for (int r = 0; r < 16; ++r) a += s[kb][r];
+    return a;
+}
+// exp2 of one query block's scores (already relative to the old reference)
+// against a reference moved up by delta, in place.
+__device__ __forceinline__ void tile_exp(f32x16 (&s)[kBN / 32], float delta) {
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r] - delta);
 }
 
-// bf16 probabilities (B operands of the P V product, one per 16 keys) and
-// their row sums, split into kBN / 4 pieces of one pair each: piece i
-// converts keys 2i, 2i+1 of fragment i / 4 and adds their fp32 values to the
-// row sum.  (Plain fp32 adds co-issue with the MFMAs; the packed bf16 dot
-// product that would add the rounded values instead shares their pipe.  The
-// two sums differ by at most 2^-9 relative per term.)
+// bf16 probabilities (B operands of the P V product, one per 16 keys), split
+// into kBN / 4 pieces of one pair each: piece i converts keys 2i, 2i+1 of
+// fragment i / 4.  (The row sums add the fp32 probabilities when they are
+// computed: plain fp32 adds co-issue with the MFMAs, while the packed bf16 dot
+// product that would add the rounded values shares their pipe.  The two sums
+// differ by at most 2^-9 relative per term.)
 struct PackedP {
     uint32_t w[kBN / 16][4];  // bf16 pairs of the B operand of 16-key step jj
 };
 
 template <int QB>
-__device__ __forceinline__ void pack_piece(const f32x16 (&pf)[QB][kBN / 32], PackedP (&pp)[QB], float (&rs)[QB],
-                                           int i) {
+__device__ __forceinline__ void pack_piece(const f32x16 (&pf)[QB][kBN / 32], PackedP (&pp)[QB], int i) {
     const int jj = i >> 2, m = i & 3;
     const int kb = jj >> 1, r = 8 * (jj & 1) + 2 * m;
 #pragma unroll
@@ -351,10 +370,7 @@ __device__ __forceinline__ void pack_piece(const f32x16 (&pf)[QB][kBN / 32], Pac
         const f32x2 x = {pf[qb][kb][r], pf[qb][kb][r + 1]};
         const bf16x2 pr = __builtin_convertvector(x, bf16x2);
         pp[qb].w[jj][m] = __builtin_bit_cast(uint32_t, pr);
-        rs[qb] += x[0];
-        rs[qb] += x[1];
         pin(pp[qb].w[jj][m]);
-        pin(rs[qb]);
     }
 }
 
@@ -408,7 +424,7 @@ template <int D, int NW, int QB, bool PACK>
 __device__ __forceinline__ void score_slots(WaveState<D, QB>& st, const LDS_AS char* __restrict__ kt,
                                             const LDS_AS char* __restrict__ vt, f32x16 (&s)[QB][kBN / 32],
                                             bf16x8 (&vf)[WaveState<D, QB>::DBLK * (kBN / 16)],
-                                            const f32x16 (&pf)[QB][kBN / 32], PackedP (&pp)[QB], float (&rs)[QB],
+                                            const f32x16 (&pf)[QB][kBN / 32], PackedP (&pp)[QB],
                                             const TileJob<D, NW, false>& kjob, const TileJob<D, NW, true>& vjob,
                                             int wave) {
     constexpr int KSEG = TileCopy<D, NW, false>::kPerWave;
@@ -424,8 +440,8 @@ __device__ __forceinline__ void score_slots(WaveState<D, QB>& st, const LDS_AS c
     for (int i = 0; i < kKAhead; ++i) read_k(st, kt, kf, i);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        s[qb][0] = f32x16{};
-        s[qb][1] = f32x16{};
+        s[qb][0] = st.negm[qb];
+        s[qb][1] = st.negm[qb];
     }
     slot_fence();
 #pragma unroll
@@ -440,7 +456,7 @@ __device__ __forceinline__ void score_slots(WaveState<D, QB>& st, const LDS_AS c
             vf[nx - NS] = v_fragment<D>(vt, st.voff[(nx - NS) % DBLK], (nx - NS) / DBLK);
         if constexpr (PACK) {
 #pragma unroll
-            for (int pc = 0; pc < PPS; ++pc) pack_piece<QB>(pf, pp, rs, i * PPS + pc);
+            for (int pc = 0; pc < PPS; ++pc) pack_piece<QB>(pf, pp, i * PPS + pc);
             // tile copies for the next step, one segment per slot so that the
             // vector-memory queue never holds up the wave
             if (i < KSEG)
@@ -472,24 +488,21 @@ __device__ __forceinline__ void value_slot(WaveState<D, QB>& st, const LDS_AS ch
 // fp32 probabilities of tile j (against the current references); on exit
 // those of tile j+1.  Two MFMA streams, each with independent VALU work in
 // its slots:
-//   scores:  S(j+1) = K(j+1) Q^T          || bf16 P(j) and its row sums
-//   values:  O += V(j)^T P(j)^T            || row max (first DBLK slots),
-//                                             exp2 of S(j+1) (the rest)
+//   scores:  S(j+1) = K(j+1) Q^T          || bf16 P(j)
+//   values:  O += V(j)^T P(j)^T            || exp2 of S(j+1) and its row sums
 // plus the copies of K(j+2) and V(j+1) into the buffers read in step j-1.
 template <int D, int NW, int QB, bool TEXT>
 __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)[QB][kBN / 32],
                                               const LDS_AS char* __restrict__ k_next,
                                               const LDS_AS char* __restrict__ v_cur, LDS_AS char* __restrict__ k_fill,
                                               LDS_AS char* __restrict__ v_fill, const KeyRange& kr, size_t row_stride,
-                                              int j, float c, int wave, int lane) {
+                                              int j, int wave, int lane) {
     constexpr int DBLK = WaveState<D, QB>::DBLK;
     constexpr int NV = DBLK * (kBN / 16);
-    constexpr int NE = NV - DBLK;                    // exp slots
-    constexpr int EPS = (QB * kBN / 2 + NE - 1) / NE;  // exp2 per exp slot (the last ones may take fewer)
     // keep the per-lane bases opaque to loop-invariant code motion: offsets
     // derived from them by XOR / add with constants are cheaper to recompute
     // each step than to hold in registers across the loop
-    asm volatile("" : "+v"(st.koff0), "+v"(st.kcopy), "+v"(st.vcopy));
+    asm volatile("" : "+v"(st.koff0));
     const int h = lane >> 5;
     apply_pending_rescale(st);
     const TileJob<D, NW, false> kjob = tile_job<D, NW, false, TEXT>(kr, st.kcopy, row_stride, j + 2, k_fill);
@@ -497,70 +510,60 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
     slot_fence();
     // scores stream
     PackedP pp[QB];
-    float rs[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) rs[qb] = 0.f;
     f32x16 s[QB][kBN / 32];
     bf16x8 vf[NV];
-    score_slots<D, NW, QB, true>(st, k_next, v_cur, s, vf, pf, pp, rs, kjob, vjob, wave);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += rs[qb];
+    score_slots<D, NW, QB, true>(st, k_next, v_cur, s, vf, pf, pp, kjob, vjob, wave);
     const int lim = kr.limit<TEXT>(j + 1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mask_tail(s[qb], lim, h);
     slot_fence();
-    // values stream, first DBLK slots: row maxes of S(j+1), a quarter of the
-    // scores per slot
-    float mx[QB];
+    // values stream: exp2 of S(j+1) against the current reference, EPS2
+    // scores per slot, and their row sums
+    float rsn[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
+    for (int qb = 0; qb < QB; ++qb) rsn[qb] = 0.f;
+    constexpr int EPS2 = QB * (kBN / 2) / NV;
+    static_assert(EPS2 * NV == QB * (kBN / 2), "exp2 work must split evenly over the value slots");
 #pragma unroll
-    for (int i = 0; i < DBLK; ++i) {
+    for (int i = 0; i < NV; ++i) {
         value_slot(st, v_cur, pp, vf, i);
-        constexpr int PER = 16 / DBLK;  // accumulator rows of each 32-key block per slot
-        static_assert(PER * DBLK == 16, "the row max must split evenly over the first value slots");
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int e = i * EPS2; e < (i + 1) * EPS2; ++e) {
+            const int qb = e / (kBN / 2), kb = (e / 16) % 2, r = e % 16;
+            s[qb][kb][r] = __builtin_amdgcn_exp2f(s[qb][kb][r]);
+            rsn[qb] += s[qb][kb][r];
+            pin(s[qb][kb][r]);
+        }
 #pragma unroll
-            for (int r = i * PER; r < (i + 1) * PER; ++r)
-                mx[qb] = fmaxf(fmaxf(mx[qb], s[qb][0][r]), s[qb][1][r]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) pin(mx[qb]);
+        for (int qb = 0; qb < QB; ++qb) pin(rsn[qb]);
         slot_fence();
     }
-    // The reference moves only when some lane's own 32 scores exceed it by
-    // more than kRescaleLog2 (base 2): the lane pair of a query shares one
-    // reference, and each lane's probabilities stay below 2^kRescaleLog2 as
-    // long as its own maximum does.  The exact pair maximum, the one exchange
-    // between the two lanes, is only needed on that rare path.
-    bool any_grow = false;
+    // A lane's probabilities are at most its tile sum: as long as no sum
+    // exceeds 2^kRescaleLog2, no probability does.  Otherwise (rare) the tile's
+    // scores are computed again from K(j+1), still in the LDS, and the
+    // reference moves to their exact pair maximum.
+    bool big = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) any_grow |= (mx[qb] - st.m_ref[qb]) * c > kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(any_grow) != 0) {
+    for (int qb = 0; qb < QB; ++qb) big |= rsn[qb] > kSumLimit;
+    if (__builtin_amdgcn_ballot_w64(big) != 0) {
+        bf16x8 vf_unused[NV];
+        PackedP pp_unused[QB];
+        const TileJob<D, NW, false> kj_unused(st.kcopy, kr.kw, row_stride, 0, 0, k_fill);
+        const TileJob<D, NW, true> vj_unused(st.vcopy, kr.vw, row_stride, 0, 0, v_fill);
+        score_slots<D, NW, QB, false>(st, k_next, k_next, s, vf_unused, s, pp_unused, kj_unused, vj_unused, wave);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const float mxp = pair_max(mx[qb]);
-            const bool grow = (mxp - st.m_ref[qb]) * c > kRescaleLog2;  // equal in both lanes of the pair
-            st.alpha[qb] = move_reference(st, qb, mxp, grow, c);
+            mask_tail(s[qb], lim, h);
+            const float mxp = tile_max(s[qb]);
+            const float delta = mxp > 0.f ? mxp : 0.f;  // equal in both lanes of the pair
+            st.alpha[qb] = move_reference(st, qb, delta);
+            tile_exp(s[qb], delta);
+            rsn[qb] = tile_sum(s[qb]);
         }
         st.pending = true;
     }
-    slot_fence();
-    // values stream, remaining slots: exp2 of S(j+1), EPS scores per slot
 #pragma unroll
-    for (int i = DBLK; i < NV; ++i) {
-        value_slot(st, v_cur, pp, vf, i);
-        const int e0 = (i - DBLK) * EPS;
-#pragma unroll
-        for (int e = e0; e < e0 + EPS; ++e) {
-            if (e < QB * kBN / 2) {
-                const int qb = e / (kBN / 2), kb = (e / 16) % 2, r = e % 16;
-                s[qb][kb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], c, -st.mc[qb]));
-                pin(s[qb][kb][r]);
-            }
-        }
-        slot_fence();
-    }
+    for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += rsn[qb];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -585,16 +588,11 @@ __device__ __forceinline__ void final_pv(WaveState<D, QB>& st, const f32x16 (&pf
     constexpr int NV = DBLK * (kBN / 16);
     apply_pending_rescale(st);
     PackedP pp[QB];
-    float rs[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) rs[qb] = 0.f;
     bf16x8 vf[NV];
 #pragma unroll
     for (int i = 0; i < kVAhead; ++i) vf[i] = v_fragment<D>(v_cur, st.voff[i % DBLK], i / DBLK);
 #pragma unroll
-    for (int i = 0; i < kBN / 4; ++i) pack_piece<QB>(pf, pp, rs, i);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += rs[qb];
+    for (int i = 0; i < kBN / 4; ++i) pack_piece<QB>(pf, pp, i);
     slot_fence();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -665,8 +663,17 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     const float c = p.scale_log2;
 
     St st;
-    st.kcopy = TileCopy<D, NW, false>::src_off0(row_stride, wave, lane);
-    st.vcopy = TileCopy<D, NW, true>::src_off0(row_stride, wave, lane);
+    {
+        const uint32_t k0off = TileCopy<D, NW, false>::src_off0(row_stride, wave, lane);
+        const uint32_t v0off = TileCopy<D, NW, true>::src_off0(row_stride, wave, lane);
+#pragma unroll
+        for (int i = 0; i < TileCopy<D, NW, false>::kPerWave; ++i) {
+            st.kcopy[i] = k0off ^ TileCopy<D, NW, false>::chunk_xor(i);
+            asm volatile("" : "+v"(st.kcopy[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < TileCopy<D, NW, true>::kPerWave; ++i) st.vcopy[i] = v0off ^ TileCopy<D, NW, true>::chunk_xor(i);
+    }
     const int nkv = kr.tiles<TEXT>();
     // V rows past the window end are never loaded: the V buffers start as
     // zeros (each wave clears the segments its own copies write, and waits for
@@ -692,7 +699,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
         const int qr_c = qr < nq ? qr : nq - 1;
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(qsrc + (size_t)qr_c * row_stride);
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) st.qf[qb][t] = qp[2 * t + h];
+        for (int t = 0; t < KSTEPS; ++t) {
+            const bf16x8 x = qp[2 * t + h];
+            f32x8 y = __builtin_convertvector(x, f32x8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= c;
+            st.qf[qb][t] = __builtin_convertvector(y, bf16x8);
+        }
     }
     // K (A operand of S^T): lane reads row r = lane % 32 of a 32-key block,
     // logical chunk 2t + h, stored at chunk (2t + h) ^ (r % kCPR).  The t
@@ -717,8 +730,8 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        st.m_ref[qb] = 0.f;
         st.mc[qb] = 0.f;
+        st.negm[qb] = f32x16{};
         st.l_run[qb] = 0.f;
         st.alpha[qb] = 1.f;
 #pragma unroll
@@ -738,16 +751,16 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     if (active) {
         bf16x8 vf_unused[DBLK * (kBN / 16)];
         PackedP pp_unused[QB];
-        float rs_unused[QB];
         const TileJob<D, NW, false> kj_unused(st.kcopy, kr.kw, row_stride, 0, 0, k1);
         const TileJob<D, NW, true> vj_unused(st.vcopy, kr.vw, row_stride, 0, 0, v1);
-        score_slots<D, NW, QB, false>(st, k0, k0, pf, vf_unused, pf, pp_unused, rs_unused, kj_unused, vj_unused,
-                                      wave);
+        score_slots<D, NW, QB, false>(st, k0, k0, pf, vf_unused, pf, pp_unused, kj_unused, vj_unused, wave);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             mask_tail(pf[qb], kr.limit<TEXT>(0), h);
-            move_reference(st, qb, tile_max(pf[qb]), true, c);  // first reference: the tile max (O is still zero)
-            tile_exp(pf[qb], c, st.mc[qb]);
+            const float mx0 = tile_max(pf[qb]);
+            move_reference(st, qb, mx0);  // first reference: the tile max (O is still zero)
+            tile_exp(pf[qb], mx0);
+            st.l_run[qb] = tile_sum(pf[qb]);
         }
     }
 
@@ -760,13 +773,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (active)
-            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, c, wave, lane);
+            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, wave, lane);
         else
             copy_step<D, NW, QB, TEXT>(st, k0, v1, kr, row_stride, j, wave);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (active)
-            pipeline_step<D, NW, QB, TEXT>(st, pf, k0, v1, k1, v0, kr, row_stride, j + 1, c, wave, lane);
+            pipeline_step<D, NW, QB, TEXT>(st, pf, k0, v1, k1, v0, kr, row_stride, j + 1, wave, lane);
         else
             copy_step<D, NW, QB, TEXT>(st, k1, v0, kr, row_stride, j + 1, wave);
     }
@@ -774,7 +787,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     __syncthreads();
     if (j + 1 < nkv) {  // one more full step (tiles j, j+1), then the P V of tile j+1
         if (active)
-            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, c, wave, lane);
+            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, wave, lane);
         else
             copy_step<D, NW, QB, TEXT>(st, k0, v1, kr, row_stride, j, wave);
         __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -818,7 +831,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
                 }
             if (p.lse && h == 0) {
                 // sum_k exp(scale * s_k) = exp(scale * m_ref) * l_tot
-                p.lse[((size_t)b * p.heads + head) * p.L + start + qr] = st.m_ref[qb] * p.scale + logf(l_tot);
+                p.lse[((size_t)b * p.heads + head) * p.L + start + qr] = st.mc[qb] * 0.6931471805599453f + logf(l_tot);
             }
         }
     }
