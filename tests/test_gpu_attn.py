@@ -44,6 +44,52 @@ def test_ragged_segments_full_compare(D, lengths):
     assert_close_full(o, lse, ref_o, ref_lse, lse_bound_windows(qh, kh, cu))
 
 
+def _steer_scores(q, k, cu, pattern):
+    """Make channel 0 decide the score trend along each window's keys: every
+    query gets q_0 = 2 and key j (0-based inside its window) gets
+      grow:   k_0 = j       (scores climb about 16 powers of two per key tile,
+                             so the reference moves in every tile),
+      jump:   k_0 = 3000 at one key in the middle of the window, else 0
+              (exp2 against the old reference overflows: only the recompute
+              from the K tile gives a finite result),
+      shrink: k_0 = -j      (later tiles underflow; the reference never moves).
+    Values are set on host copies and cast to bf16, so the oracle reads the
+    same bytes."""
+    qf, kf = q.float().cpu(), k.float().cpu()
+    qf[..., 0] = 2.0
+    for i in range(len(cu) - 1):
+        a, e = int(cu[i]), int(cu[i + 1])
+        j = torch.arange(e - a, dtype=torch.float32)
+        if pattern == "grow":
+            kf[:, a:e, :, 0] = j[None, :, None]
+        elif pattern == "shrink":
+            kf[:, a:e, :, 0] = -j[None, :, None]
+        else:
+            kf[:, a:e, :, 0] = 0.0
+            if e > a:
+                kf[:, a + (e - a) // 2 + 3 if (e - a) // 2 + 3 < e - a else a, :, 0] = 3000.0
+    return qf.to(torch.bfloat16).to(q.device), kf.to(torch.bfloat16).to(k.device)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("pattern", ["grow", "jump", "shrink"])
+def test_reference_moves(D, pattern):
+    """Score trends that move (or never move) the softmax reference, checked
+    element by element against the oracle: several key tiles, a window of
+    exactly one tile, and one shorter than a tile."""
+    say(f"reference moves D={D} pattern={pattern}")
+    lengths = [700, 64, 130, 5]
+    cu = _cu(lengths)
+    L, B, Hh = int(cu[-1]), 1, 2
+    q, k, v = (normal((B, L, Hh, D), 520 + t, device=DEV) for t in range(3))
+    q, k = _steer_scores(q, k, cu, pattern)
+    o, lse = wa.attn_fwd(q, k, v, torch.as_tensor(cu, device=DEV), max(lengths), return_lse=True)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    qh, kh = to_f64(q), to_f64(k)
+    ref_o, ref_lse = oatt.window_attention(qh, kh, to_f64(v), cu)
+    assert_close_full(o, lse, ref_o, ref_lse, lse_bound_windows(qh, kh, cu))
+
+
 def test_rows_outside_windows_untouched_and_empty_plan():
     D, Hh, L = 128, 2, 96
     q, k, v = (normal((1, L, Hh, D), 600 + t, device=DEV) for t in range(3))

@@ -64,6 +64,38 @@ def test_small_full_compare(D, lengths, T):
                 assert np.all(np.abs(got - ref_lse) <= lse_bound(qh[b, a:e, h], ks, s))
 
 
+@pytest.mark.parametrize("where", ["window", "text"])
+def test_reference_moves_with_text(where):
+    """Scores that climb along the keys, in the window rows or in the text
+    rows, so that the softmax reference moves inside window tiles or inside
+    text tiles (checked against the oracle element by element)."""
+    B, Hh, D, T = 1, 2, 128, 150
+    lengths = [300, 64, 7]
+    cu = _cu(lengths)
+    L = int(cu[-1])
+    q, k, v = (normal((B, L, Hh, D), 540 + t, device=DEV) for t in range(3))
+    tq, tk, tv = _text(B, T, Hh, D, 560)
+    qf, kf, tqf, tkf = (x.float().cpu() for x in (q, k, tq, tk))
+    qf[..., 0] = 2.0
+    tqf[..., 0] = 2.0
+    if where == "window":
+        for i in range(len(lengths)):
+            a, e = int(cu[i]), int(cu[i + 1])
+            kf[:, a:e, :, 0] = torch.arange(e - a, dtype=torch.float32)[None, :, None]
+        tkf[..., 0] = 0.0
+    else:
+        kf[..., 0] = 0.0
+        tkf[..., 0] = torch.arange(T, dtype=torch.float32)[None, :, None]
+    q, k, tq, tk = (x.to(torch.bfloat16).to(DEV) for x in (qf, kf, tqf, tkf))
+    cu_d = torch.as_tensor(cu, device=DEV)
+    o, to = wa.attn_fwd_text(q, k, v, cu_d, max(lengths), tq, tk, tv)
+    torch.cuda.synchronize()
+    qh, kh, vh, tqh, tkh, tvh = (to_f64(x) for x in (q, k, v, tq, tk, tv))
+    ref_o, ref_t, _ = otxt.text_window_attention(qh, kh, vh, cu.tolist(), tqh, tkh, tvh)
+    _close(o, ref_o, "video")
+    _close(to, ref_t, "text")
+
+
 def test_no_text_is_plain_window_attention_bit_for_bit():
     B, Hh, D = 1, 3, 128
     cu = _cu([1, 130, 64, 257])

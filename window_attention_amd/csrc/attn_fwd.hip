@@ -13,10 +13,10 @@
 //     v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator layout a lane holds
 //     16 keys of ONE query column (lane % 32), so the softmax row max and row
 //     sum are in-lane reductions plus one exchange with lane ^ 32.
-//   * The softmax runs in base 2 on scores relative to a per-row reference
-//     m: Q is loaded as bf16(q * scale * log2 e), and every score chain
-//     starts from the accumulator value -m, so the MFMAs produce
-//     scale * log2(e) * q.k - m directly and a probability costs one exp2.
+//   * The softmax runs in base 2: a probability is exp2(c * s - mc) with
+//     c = scale * log2(e), s the fp32 score from the MFMAs (bf16 products
+//     are exact, sums in fp32) and mc a per-row reference, one fma and one
+//     exp2 per score.
 //   * O^T = V^T P^T with the same instruction.  P^T is used straight from the
 //     score registers as the B operand: the 8 keys a lane supplies for a
 //     16-key step are the ones its accumulator already holds (keys
@@ -246,21 +246,20 @@ __device__ __forceinline__ TileJob<D, NW, IS_V> tile_job(const KeyRange& kr, con
 }
 
 // Running state of one wave: QB blocks of 32 query rows, online softmax in
-// base 2.  With c = softmax_scale * log2(e), the score of query q and key k
-// is x = c q.k (Q enters as bf16(c q)) and its probability exp2(x - mc), mc
-// a reference that no tile's probabilities exceed by much (see kSumLimit).
+// base 2.  With c = softmax_scale * log2(e), the probability of score s is
+// exp2(c s - mc), mc a reference that no tile's probabilities exceed by much
+// (see kSumLimit).
 template <int D, int QB>
 struct WaveState {
     static constexpr int KSTEPS = D / 16;
     static constexpr int DBLK = D / 32;
     bf16x8 qf[QB][KSTEPS];  // Q fragments, B operands of S^T = K Q^T
     f32x16 oacc[QB][DBLK];  // O^T accumulators: column = this lane's query
-    float mc[QB];           // reference of the scores x (equal in lanes l and l ^ 32)
-    f32x16 negm[QB];        // -mc in every accumulator register: the score chains start from it
+    float mc[QB];           // reference, in units of c * s (equal in lanes l and l ^ 32)
     float l_run[QB];        // sum of the fp32 probabilities this lane contributed
     float alpha[QB];        // O rescale factor owed since the reference last moved
     bool pending;           // wave-uniform: alpha must be applied before the next P V
-    int koff0;              // LDS byte offset of the K operand at k step 0 (step t: ^ 32 t)
+    int koff[KSTEPS];       // LDS byte offsets of the K operand per k step
     int voff[DBLK];         // LDS byte offsets of the transposed V reads per O^T block
     // source offsets of this lane's K and V tile segments (the first
     // TileCopy::kPerWave entries are used)
@@ -274,7 +273,7 @@ struct WaveState {
 template <int D, int QB>
 __device__ __forceinline__ bf16x8 k_fragment(const WaveState<D, QB>& st, const LDS_AS char* __restrict__ kt, int i) {
     using Ly = Layout<D>;
-    return *reinterpret_cast<const LDS_AS bf16x8*>(kt + (i & 1) * 32 * Ly::kRowBytes + (st.koff0 ^ (32 * (i >> 1))));
+    return *reinterpret_cast<const LDS_AS bf16x8*>(kt + (i & 1) * 32 * Ly::kRowBytes + st.koff[i >> 1]);
 }
 
 // Instruction slots.  The key loop is laid out by hand as a sequence of
@@ -320,15 +319,12 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[kBN / 32]) {
 }
 
 // Move the reference of query block qb up by delta (0 in lanes whose
-// reference stays), rebasing the running sum and the value the score chains
-// start from.  Returns the factor O must be multiplied by once every earlier
-// P V product is in it.
+// reference stays) and rebase the running sum.  Returns the factor O must be
+// multiplied by once every earlier P V product is in it.
 template <int D, int QB>
 __device__ __forceinline__ float move_reference(WaveState<D, QB>& st, int qb, float delta) {
     const float alpha = __builtin_amdgcn_exp2f(-delta);
     st.mc[qb] += delta;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.negm[qb][r] = -st.mc[qb];
     st.l_run[qb] *= alpha;
     return alpha;
 }
@@ -342,13 +338,12 @@ __device__ __forceinline__ float tile_sum(const f32x16 (&s)[kBN / 32]) {
         for (int r = 0; r < 16; ++r) a += s[kb][r];
     return a;
 }
-// exp2 of one query block's scores (already relative to the old reference)
-// against a reference moved up by delta, in place.
-__device__ __forceinline__ void tile_exp(f32x16 (&s)[kBN / 32], float delta) {
+// exp2 of one query block's raw scores against its reference, in place.
+__device__ __forceinline__ void tile_exp(f32x16 (&s)[kBN / 32], float c, float mc) {
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r] - delta);
+        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mc));
 }
 
 // bf16 probabilities (B operands of the P V product, one per 16 keys), split
@@ -440,8 +435,8 @@ __device__ __forceinline__ void score_slots(WaveState<D, QB>& st, const LDS_AS c
     for (int i = 0; i < kKAhead; ++i) read_k(st, kt, kf, i);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        s[qb][0] = st.negm[qb];
-        s[qb][1] = st.negm[qb];
+        s[qb][0] = f32x16{};
+        s[qb][1] = f32x16{};
     }
     slot_fence();
 #pragma unroll
@@ -496,13 +491,9 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
                                               const LDS_AS char* __restrict__ k_next,
                                               const LDS_AS char* __restrict__ v_cur, LDS_AS char* __restrict__ k_fill,
                                               LDS_AS char* __restrict__ v_fill, const KeyRange& kr, size_t row_stride,
-                                              int j, int wave, int lane) {
+                                              int j, float c, int wave, int lane) {
     constexpr int DBLK = WaveState<D, QB>::DBLK;
     constexpr int NV = DBLK * (kBN / 16);
-    // keep the per-lane bases opaque to loop-invariant code motion: offsets
-    // derived from them by XOR / add with constants are cheaper to recompute
-    // each step than to hold in registers across the loop
-    asm volatile("" : "+v"(st.koff0));
     const int h = lane >> 5;
     apply_pending_rescale(st);
     const TileJob<D, NW, false> kjob = tile_job<D, NW, false, TEXT>(kr, st.kcopy, row_stride, j + 2, k_fill);
@@ -530,7 +521,7 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
 #pragma unroll
         for (int e = i * EPS2; e < (i + 1) * EPS2; ++e) {
             const int qb = e / (kBN / 2), kb = (e / 16) % 2, r = e % 16;
-            s[qb][kb][r] = __builtin_amdgcn_exp2f(s[qb][kb][r]);
+            s[qb][kb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], c, -st.mc[qb]));
             rsn[qb] += s[qb][kb][r];
             pin(s[qb][kb][r]);
         }
@@ -554,10 +545,10 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             mask_tail(s[qb], lim, h);
-            const float mxp = tile_max(s[qb]);
+            const float mxp = fmaf(tile_max(s[qb]), c, -st.mc[qb]);
             const float delta = mxp > 0.f ? mxp : 0.f;  // equal in both lanes of the pair
             st.alpha[qb] = move_reference(st, qb, delta);
-            tile_exp(s[qb], delta);
+            tile_exp(s[qb], c, st.mc[qb]);
             rsn[qb] = tile_sum(s[qb]);
         }
         st.pending = true;
@@ -699,21 +690,21 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
         const int qr_c = qr < nq ? qr : nq - 1;
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(qsrc + (size_t)qr_c * row_stride);
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-            const bf16x8 x = qp[2 * t + h];
-            f32x8 y = __builtin_convertvector(x, f32x8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] *= c;
-            st.qf[qb][t] = __builtin_convertvector(y, bf16x8);
-        }
+        for (int t = 0; t < KSTEPS; ++t) st.qf[qb][t] = qp[2 * t + h];
     }
     // K (A operand of S^T): lane reads row r = lane % 32 of a 32-key block,
     // logical chunk 2t + h, stored at chunk (2t + h) ^ (r % kCPR).  The t
     // part only flips chunk bits above bit 0, so the offset of step t is the
-    // step-0 offset XOR 32 t.
+    // step-0 offset XOR 32 t.  (Kept opaque so that the compiler holds them
+    // rather than recomputing them in the loop.)
     {
         const int r = lane & 31;
-        st.koff0 = r * Ly::kRowBytes + Ly::k_chunk(r, h) * 16;
+        const int koff0 = r * Ly::kRowBytes + Ly::k_chunk(r, h) * 16;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            st.koff[t] = koff0 ^ (32 * t);
+            asm volatile("" : "+v"(st.koff[t]));
+        }
     }
     // V (A operand of O^T, transposed read): address-supplying lane s of
     // 16-lane group g points at row 4*(g/2) + e, column 16*(g%2) + 4*c of a
@@ -731,7 +722,6 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         st.mc[qb] = 0.f;
-        st.negm[qb] = f32x16{};
         st.l_run[qb] = 0.f;
         st.alpha[qb] = 1.f;
 #pragma unroll
@@ -757,9 +747,8 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             mask_tail(pf[qb], kr.limit<TEXT>(0), h);
-            const float mx0 = tile_max(pf[qb]);
-            move_reference(st, qb, mx0);  // first reference: the tile max (O is still zero)
-            tile_exp(pf[qb], mx0);
+            move_reference(st, qb, tile_max(pf[qb]) * c);  // first reference: the tile max (O is still zero)
+            tile_exp(pf[qb], c, st.mc[qb]);
             st.l_run[qb] = tile_sum(pf[qb]);
         }
     }
@@ -773,13 +762,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (active)
-            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, wave, lane);
+            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, c, wave, lane);
         else
             copy_step<D, NW, QB, TEXT>(st, k0, v1, kr, row_stride, j, wave);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (active)
-            pipeline_step<D, NW, QB, TEXT>(st, pf, k0, v1, k1, v0, kr, row_stride, j + 1, wave, lane);
+            pipeline_step<D, NW, QB, TEXT>(st, pf, k0, v1, k1, v0, kr, row_stride, j + 1, c, wave, lane);
         else
             copy_step<D, NW, QB, TEXT>(st, k1, v0, kr, row_stride, j + 1, wave);
     }
@@ -787,7 +776,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     __syncthreads();
     if (j + 1 < nkv) {  // one more full step (tiles j, j+1), then the P V of tile j+1
         if (active)
-            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, wave, lane);
+            pipeline_step<D, NW, QB, TEXT>(st, pf, k1, v0, k0, v1, kr, row_stride, j, c, wave, lane);
         else
             copy_step<D, NW, QB, TEXT>(st, k0, v1, kr, row_stride, j, wave);
         __builtin_amdgcn_s_waitcnt(0x0F70);
