@@ -351,7 +351,7 @@ __device__ __forceinline__ void tile_exp(f32x16 (&s)[kBN / 32], float c, float m
 // fragment i / 4.  (The row sums add the fp32 probabilities when they are
 // computed: plain fp32 adds co-issue with the MFMAs, while the packed bf16 dot
 // product that would add the rounded values shares their pipe.  The two sums
-// differ by at most 2^-9 relative per term.)
+// differ by at most 2^-8 relative per term.)
 struct PackedP {
     uint32_t w[kBN / 16][4];  // bf16 pairs of the B operand of 16-key step jj
 };
