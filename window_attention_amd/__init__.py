@@ -185,7 +185,7 @@ def plan_cached(T, H, W, nt, nh, nw, method=REGULAR, device=None) -> Plan:
     """``plan`` behind an LRU cache keyed on the grid, the window counts, the
     method and the device (a plan is a pure function of these)."""
     import torch
-    dev = None if device is None else str(torch.device(device))
+    dev = str(torch.device("cpu" if device is None else device))  # None means host tables, as "cpu"
     key = (T, H, W, nt, nh, nw, method, dev)
     p = _PLAN_CACHE.get(key)
     if p is not None:
