@@ -503,7 +503,13 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
     PackedP pp[QB];
     f32x16 s[QB][kBN / 32];
     bf16x8 vf[NV];
+    // The two waves of a SIMD run independent workgroups.  The one in its
+    // value half (MFMAs plus all the exp2 and row-sum work) gets issue
+    // priority over one in its score half (MFMAs plus light VALU), which
+    // fills the gaps: about 2.5 % on a regular layer.
+    __builtin_amdgcn_s_setprio(0);
     score_slots<D, NW, QB, true>(st, k_next, v_cur, s, vf, pf, pp, kjob, vjob, wave);
+    __builtin_amdgcn_s_setprio(1);
     const int lim = kr.limit<TEXT>(j + 1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mask_tail(s[qb], lim, h);
