@@ -40,7 +40,9 @@
 //     The loop is laid out by hand in slots of one MFMA each, with the LDS
 //     reads of an operand issued a few MFMAs before its use and scheduling
 //     fences between slots, so that an MFMA never waits for a read issued
-//     just before it.
+//     just before it.  Two workgroups share a CU (one wave of each per
+//     SIMD); a wave in its value half takes issue priority over one in its
+//     score half.
 //   * Grid: blockIdx % 8 selects the XCD; all query tiles of one (batch,
 //     window, head) go to the same XCD, consecutively, so they share its L2
 //     while they stream the same K/V tiles.
