@@ -21,5 +21,7 @@ extern "C" const char* win_strerror(int status) {
 extern "C" const char* win_build_info(void) {
     return "winattn gfx950 | plan: closed-form host + device fill | permute: wave-per-row 16B lanes, "
            "non-temporal | attn_fwd: S^T=KQ^T and O^T=V^TP^T on mfma_f32_32x32x16_bf16, 4 waves x 32 query rows, "
-           "64-key tiles, global_load_lds double buffer, ds_read_b64_tr_b16 for V, xcd-grouped grid";
+           "64-key tiles, buffer_load lds double buffer, ds_read_b64_tr_b16 for V, base-2 softmax with a row-sum "
+           "overflow check (no row max), value-half issue priority, xcd-grouped grid | rope: fused into the "
+           "permute | text: [window | text] key tiles, fp32 per-window workspace";
 }
