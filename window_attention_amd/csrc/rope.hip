@@ -62,6 +62,25 @@ struct RopeArgs {
     int32_t ext[3];           // window extents on t, h, w (rows of the table per axis)
 };
 
+// This lane's four (cos, sin) pairs, the same in every head of the row.  The
+// row's three window-local coordinates are wave-uniform (scalar loads); a
+// lane picks the one of its pairs' axis.
+__device__ __forceinline__ void row_rotation(const RopeArgs& a, int32_t j, uint32_t lane, f32x2 (&cs)[4],
+                                             bool (&rot)[4]) {
+    const int32_t loc[3] = {clamp_to(a.local[3 * j], a.ext[0]), clamp_to(a.local[3 * j + 1], a.ext[1]),
+                            clamp_to(a.local[3 * j + 2], a.ext[2])};
+    const int32_t cb = (int32_t)lane % a.head_chunks;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int32_t p = cb * 4 + q;
+        rot[q] = p < a.span_pairs;
+        const int32_t axis = rot[q] ? p / a.axis_pairs : 0;
+        const int32_t i = rot[q] ? p - axis * a.axis_pairs : 0;
+        const int32_t row = axis == 0 ? loc[0] : (axis == 1 ? a.ext[0] + loc[1] : a.ext[0] + a.ext[1] + loc[2]);
+        cs[q] = a.table[row * a.axis_pairs + i];
+    }
+}
+
 __global__ __launch_bounds__(64) void rope_rows_kernel(RopeArgs a) {
     const uint32_t lane = threadIdx.x;
     const uint32_t r = blockIdx.x;
@@ -71,20 +90,8 @@ __global__ __launch_bounds__(64) void rope_rows_kernel(RopeArgs a) {
     const int32_t jj = a.perm_dst ? clamp_to(a.idx[clamp_to(a.perm_dst[j], a.L)], a.L) : clamp_to(a.idx[j], a.L);
     const u32x4* s = a.src + ((uint64_t)b * a.L + jj) * a.cpr;
     u32x4* d = a.dst + (uint64_t)r * a.cpr;
-    // this lane's four channel pairs, the same in every head
-    const int32_t cb = (int32_t)lane % a.head_chunks;
     f32x2 cs[4];
     bool rot[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int32_t p = cb * 4 + q;
-        rot[q] = p < a.span_pairs;
-        const int32_t axis = rot[q] ? p / a.axis_pairs : 0;
-        const int32_t i = rot[q] ? p - axis * a.axis_pairs : 0;
-        const int32_t pos = clamp_to(a.local[3 * j + axis], a.ext[axis]);
-        const int32_t row = (axis == 0 ? 0 : (axis == 1 ? a.ext[0] : a.ext[0] + a.ext[1])) + pos;
-        cs[q] = a.table[row * a.axis_pairs + i];
-    }
     for (uint32_t c0 = 0; c0 < a.cpr; c0 += 64 * kUnroll) {
         u32x4 v[kUnroll];
 #pragma unroll
@@ -92,6 +99,8 @@ __global__ __launch_bounds__(64) void rope_rows_kernel(RopeArgs a) {
             const uint32_t c = c0 + u * 64 + lane;
             if (c < a.cpr) v[u] = __builtin_nontemporal_load(s + c);
         }
+        // the rotation's table reads go out behind the row's first loads
+        if (c0 == 0) row_rotation(a, j, lane, cs, rot);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t c = c0 + u * 64 + lane;
