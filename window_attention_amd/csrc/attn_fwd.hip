@@ -25,7 +25,9 @@
 //     lane, so V needs no transpose pass.  The O^T accumulator column is again
 //     the lane's own query, so the online-softmax rescale is per lane.
 //   * Every K or V fragment read from LDS feeds QB MFMAs (one per query
-//     block), so LDS read traffic per flop falls as 1 / QB.
+//     block), so LDS read traffic per flop falls as 1 / QB.  The library
+//     launches QB = 1: two blocks per wave need a SIMD's whole register file,
+//     one wave per SIMD, and that ran slower than two waves of one block.
 //   * K and V tiles (64 keys) are copied HBM -> LDS with
 //     buffer_load_dwordx4 ... lds (no VGPR staging), double buffered.  Rows are
 //     stored with an XOR swizzle of their 16-byte chunks so that the K reads
@@ -35,7 +37,7 @@
 //     scores run, the VALU packs tile j's probabilities; while the MFMAs of
 //     tile j's P V product run, the VALU does tile j+1's exp2 and row sums.
 //     No row max is taken on the common path: a tile's probabilities are
-//     bounded by its row sum, and only a sum above 2^kRescaleLog2 sends the
+//     bounded by its row sum, and only a sum above kSumLimit = 2^8 sends the
 //     tile down the rare path that moves the reference.
 //     The loop is laid out by hand in slots of one MFMA each, with the LDS
 //     reads of an operand issued a few MFMAs before its use and scheduling
@@ -72,9 +74,9 @@ constexpr int kBN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 // The reference of a row moves (and O is rescaled) only when some lane's
-// probabilities of one tile sum to more than 2^kRescaleLog2; every
-// probability is then at most 2^kRescaleLog2.
-constexpr float kSumLimit = 256.f;  // 2^kRescaleLog2, kRescaleLog2 = 8
+// probabilities of one tile sum to more than kSumLimit; as long as none does,
+// every probability is at most kSumLimit.
+constexpr float kSumLimit = 256.f;
 
 struct AttnParams {
     const bf16* q;
@@ -538,7 +540,7 @@ __device__ __forceinline__ void pipeline_step(WaveState<D, QB>& st, f32x16 (&pf)
         slot_fence();
     }
     // A lane's probabilities are at most its tile sum: as long as no sum
-    // exceeds 2^kRescaleLog2, no probability does.  Otherwise (rare) the tile's
+    // exceeds kSumLimit, no probability does.  Otherwise (rare) the tile's
     // scores are computed again from K(j+1), still in the LDS, and the
     // reference moves to their exact pair maximum.
     bool big = false;
