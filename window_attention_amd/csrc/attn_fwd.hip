@@ -798,15 +798,53 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
     if (!active) return;
 
     // ---- epilogue ------------------------------------------------------------
+    // O^T holds one query row per lane, so stores straight from the
+    // accumulators would put 16 bytes into each of 32 rows per instruction.
+    // The rows go through this wave's own 32-row region of the K buffers
+    // instead (idle since the last step barrier), so that every store writes
+    // whole rows: bf16 video rows in one pass, fp32 text rows in two passes of
+    // half a row.  The region keeps the tiles' chunk swizzle.  One wave's LDS
+    // accesses complete in order; the waits also keep the compiler from moving
+    // reads above the writes they depend on, or writes above earlier reads.
+    static_assert(NW * 32 * Ly::kRowBytes <= 2 * Ly::kTileBytes, "O staging must fit the K buffers");
+    LDS_AS char* const stage = k0 + wave * 32 * Ly::kRowBytes;
+    const int r0 = lane & 31;
+    const int sw0 = r0 & (Ly::kCPR - 1);
+    constexpr int kRowsPerStore = 1024 / Ly::kRowBytes;
+    const int sc = lane % Ly::kCPR;  // chunk of a row this lane stores
+    const int row0 = q0 + wave * 32 * QB;  // first query row of this wave
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qr = qrow0 + qb * 32;
         const float l_tot = pair_sum(st.l_run[qb]);
         const float inv = 1.f / l_tot;
-        if (text_rows && qr < nq) {
+        if (text_rows) {
             // this window's text output, normalized, kept in fp32 for the mean
             // over windows
-            float* trow = p.tpart + (((size_t)b * p.num_windows + win) * p.text_len + qr) * row_stride + head * D;
+            float* const tbase = p.tpart + ((size_t)b * p.num_windows + win) * p.text_len * row_stride + head * D;
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr) {
+#pragma unroll
+                for (int db = hr * DBLK / 2; db < (hr + 1) * DBLK / 2; ++db)
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        f32x4 x;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) x[i] = st.oacc[qb][db][4 * a + i] * inv;
+                        const int chunk = ((db - hr * DBLK / 2) * 8 + 2 * a + h) ^ sw0;
+                        *(LDS_AS f32x4*)(stage + r0 * Ly::kRowBytes + chunk * 16) = x;
+                    }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int t = 0; t < 32 / kRowsPerStore; ++t) {
+                    const int r = t * kRowsPerStore + lane / Ly::kCPR;
+                    const f32x4 y = *(const LDS_AS f32x4*)(stage + r * Ly::kRowBytes + (sc ^ (r & (Ly::kCPR - 1))) * 16);
+                    const int row = row0 + qb * 32 + r;
+                    if (row < nq) *reinterpret_cast<f32x4*>(tbase + (size_t)row * row_stride + hr * (D / 2) + sc * 4) = y;
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+        } else {
 #pragma unroll
             for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -814,21 +852,19 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd<QB>()) void attn_fwd_kernel
                     f32x4 x;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) x[i] = st.oacc[qb][db][4 * a + i] * inv;
-                    *reinterpret_cast<f32x4*>(trow + db * 32 + 8 * a + 4 * h) = x;
+                    *(LDS_AS bf16x4*)(stage + r0 * Ly::kRowBytes + ((db * 4 + a) ^ sw0) * 16 + h * 8) =
+                        __builtin_convertvector(x, bf16x4);
                 }
-        } else if (qr < nq) {
-            bf16* orow = p.o + base_off + (size_t)qr * row_stride;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-            for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    f32x4 x;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) x[i] = st.oacc[qb][db][4 * a + i] * inv;
-                    const bf16x4 y = __builtin_convertvector(x, bf16x4);
-                    *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * a + 4 * h) = y;
-                }
-            if (p.lse && h == 0) {
+            for (int t = 0; t < 32 / kRowsPerStore; ++t) {
+                const int r = t * kRowsPerStore + lane / Ly::kCPR;
+                const bf16x8 y = *(const LDS_AS bf16x8*)(stage + r * Ly::kRowBytes + (sc ^ (r & (Ly::kCPR - 1))) * 16);
+                const int row = row0 + qb * 32 + r;
+                if (row < nq) *reinterpret_cast<bf16x8*>(p.o + base_off + (size_t)row * row_stride + sc * 8) = y;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (p.lse && h == 0 && qr < nq) {
                 // sum_k exp(scale * s_k) = exp(scale * m_ref) * l_tot
                 p.lse[((size_t)b * p.heads + head) * p.L + start + qr] = st.mc[qb] * 0.6931471805599453f + logf(l_tot);
             }
