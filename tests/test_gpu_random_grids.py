@@ -16,7 +16,8 @@ import window_attention_amd as wa
 from oracle import attention as oatt
 from oracle import permute as operm
 from oracle import plan as oplan
-from tests.gpu_helpers import assert_close_full, lse_bound_windows, say, to_f64
+from oracle import text_attention as otxt
+from tests.gpu_helpers import MAX_ABS, MEAN_ABS, assert_close_full, lse_bound_windows, say, to_f64
 from window_attention_amd.inputs import qkv
 
 pytestmark = pytest.mark.gpu
@@ -63,3 +64,33 @@ def test_random_grid_whole_path(seed):
     ref_o, ref_lse = oatt.masked_full_attention(qh, kh, vh, win)
     tol = lse_bound_windows(operm.gather(qh, op.perm), operm.gather(kh, op.perm), op.cu_seqlens)[:, :, op.inv]
     assert_close_full(o, lse[:, :, p.inv.long()], ref_o, ref_lse, tol)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_grid_with_text(seed):
+    """The text-augmented call on the same kind of draws, with 1 to 300 text
+    rows: video rows in window order, the text output and the per-window
+    text outputs against the oracle's [window, text] segments."""
+    T, H, W, nt, nh, nw, method, batch, heads, D, sigma = _draw(1000 + seed)
+    text_len = int(np.random.default_rng(2000 + seed).integers(1, 301))
+    say(f"random grid with text seed={seed}: {T}x{H}x{W} counts {nt},{nh},{nw} method {method} B={batch} "
+        f"heads={heads} D={D} sigma={sigma} text={text_len}")
+    L = T * H * W
+    q, k, _ = qkv(200 + seed, batch, L, heads, D, sigma, device=DEV)
+    v = qkv(200 + seed, batch, L, heads, D, 1.0, device=DEV)[2]
+    tq, tk, _ = qkv(300 + seed, batch, text_len, heads, D, sigma, device=DEV)
+    tv = qkv(300 + seed, batch, text_len, heads, D, 1.0, device=DEV)[2]
+    p = wa.plan(T, H, W, nt, nh, nw, method, device=DEV)
+    qw, kw, vw = (wa.gather(x, p.perm) for x in (q, k, v))
+    ws = torch.full((batch, p.num_windows, text_len, heads, D), float("nan"), dtype=torch.float32, device=DEV)
+    ow, to = wa.attn_fwd_text(qw, kw, vw, p.cu_seqlens, p.max_seqlen, tq, tk, tv, workspace=ws)
+    torch.cuda.synchronize()
+
+    op = oplan.plan(T, H, W, nt, nh, nw, method)
+    qh, kh, vh = (operm.gather(to_f64(x), op.perm) for x in (q, k, v))
+    ref_o, ref_t, ref_per = otxt.text_window_attention(qh, kh, vh, list(op.cu_seqlens), to_f64(tq), to_f64(tk),
+                                                       to_f64(tv))
+    for got, want, what in ((to_f64(ow), ref_o, "video"), (to_f64(to), ref_t, "text"),
+                            (ws.double().cpu().numpy(), ref_per, "per-window text")):
+        err = np.abs(got - want)
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (what, float(err.max()), float(err.mean()))
