@@ -44,6 +44,28 @@ def test_ragged_segments_full_compare(D, lengths):
     assert_close_full(o, lse, ref_o, ref_lse, lse_bound_windows(qh, kh, cu))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("scale", [0.02, 0.3, 1.0])
+def test_softmax_scale(D, scale):
+    """A caller's softmax scale other than 1/sqrt(D): near-uniform rows
+    (0.02) and peaked rows whose reference moves (1.0, scores of standard
+    deviation sqrt(D)); O and the LSE, log sum_k exp(scale * s_k), against
+    the oracle with the same scale.  V has standard deviation 1/2: a peaked
+    row's output is one V row, and above 4 in magnitude the bf16 rounding of
+    the output alone (up to 2^-6) would use most of the absolute tolerance."""
+    say(f"softmax scale D={D} scale={scale}")
+    lengths = [1, 65, 200, 700]
+    cu = _cu(lengths)
+    L, B, Hh = int(cu[-1]), 1, 2
+    q, k = (normal((B, L, Hh, D), 520 + t, device=DEV) for t in range(2))
+    v = normal((B, L, Hh, D), 522, sigma=0.5, device=DEV)
+    o, lse = wa.attn_fwd(q, k, v, torch.as_tensor(cu, device=DEV), max(lengths), softmax_scale=scale,
+                         return_lse=True)
+    qh, kh = to_f64(q), to_f64(k)
+    ref_o, ref_lse = oatt.window_attention(qh, kh, to_f64(v), cu, scale)
+    assert_close_full(o, lse, ref_o, ref_lse, lse_bound_windows(qh, kh, cu, scale))
+
+
 def _steer_scores(q, k, cu, pattern):
     """Make channel 0 decide the score trend along each window's keys: every
     query gets q_0 = 2 and key j (0-based inside its window) gets

@@ -64,6 +64,25 @@ def test_small_full_compare(D, lengths, T):
                 assert np.all(np.abs(got - ref_lse) <= lse_bound(qh[b, a:e, h], ks, s))
 
 
+@pytest.mark.parametrize("scale", [0.05, 0.5])
+def test_softmax_scale_with_text(scale):
+    """A caller's softmax scale reaches the text keys and the text queries as
+    well as the window's."""
+    B, Hh, D, T = 1, 2, 128, 70
+    lengths = [130, 0, 64, 300]
+    cu = _cu(lengths)
+    L = int(cu[-1])
+    q, k, v = (normal((B, L, Hh, D), 530 + t, device=DEV) for t in range(3))
+    tq, tk, tv = _text(B, T, Hh, D, 640)
+    o, to = wa.attn_fwd_text(q, k, v, torch.as_tensor(cu, device=DEV), max(lengths), tq, tk, tv,
+                             softmax_scale=scale)
+    torch.cuda.synchronize()
+    qh, kh, vh, tqh, tkh, tvh = (to_f64(x) for x in (q, k, v, tq, tk, tv))
+    ref_o, ref_t, _ = otxt.text_window_attention(qh, kh, vh, cu.tolist(), tqh, tkh, tvh, scale)
+    _close(o, ref_o, "video")
+    _close(to, ref_t, "text")
+
+
 @pytest.mark.parametrize("where", ["window", "text"])
 def test_reference_moves_with_text(where):
     """Scores that climb along the keys, in the window rows or in the text
