@@ -883,6 +883,9 @@ __global__ __launch_bounds__(256) void text_mean_kernel(const float* __restrict_
     const int64_t b = e / per_batch, r = e - b * per_batch;
     const float* src = part + (size_t)b * num_windows * per_batch + r;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // unrolled so that several windows' loads are in flight; the adds keep
+    // window order
+#pragma unroll 8
     for (int32_t i = 0; i < num_windows; ++i) acc += *reinterpret_cast<const f32x4*>(src + (size_t)i * per_batch);
     const float w = (float)num_windows;
     const f32x4 m = {acc[0] / w, acc[1] / w, acc[2] / w, acc[3] / w};
