@@ -40,6 +40,9 @@
  *     "host" pointers are ordinary process memory.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Device work is
  *     enqueued on it asynchronously; no function synchronises the device.
+ *     Device work is kernel launches only (no allocation, no memset, no
+ *     copy), so every call may be recorded into a stream-captured HIP graph
+ *     and replayed with new data in the same buffers.
  *   - Token tensors are contiguous [B, L, row] with a 16-byte aligned base;
  *     the same plan applies to every batch element.  Attention tensors are
  *     [B, L, heads, head_dim] bf16.
