@@ -25,6 +25,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+ATTN_KERNEL = "attn_fwd_kernel<128,4,1,"  # kernel-name prefix of the traffic records
 
 
 def log(*a):
@@ -80,6 +81,30 @@ class Step:
         # one read and one write of every row, plus the index reads (4 B per
         # row for gather/scatter, 8 B for a transition)
         self.perm_bytes_data = 2 * w.batch * w.L * self.row_bytes
+
+    def permute_launches(self):
+        """The step's permute launches in order (entry gather, the fused
+        transitions, exit scatter) as closures over the step's buffers."""
+        wa, w = self.wa, self.w
+        out = []
+        cur = w.entry
+        src = self.bufs[0]
+        p = self.plans[cur]
+        for x, dst in zip((self.q, self.k, self.v), src):
+            out.append(lambda x=x, dst=dst, p=p: wa.gather(x, p.perm, out=dst))
+        side = 0
+        for lay in w.schedule:
+            if lay != cur:
+                pa, pb = self.plans[cur], self.plans[lay]
+                dst = self.bufs[1 - side]
+                for s_, d_ in zip(src, dst):
+                    out.append(lambda s_=s_, d_=d_, pa=pa, pb=pb: wa.transition(s_, pa.inv, pb.perm, out=d_))
+                side = 1 - side
+                src = dst
+                cur = lay
+        pl = self.plans[cur]
+        out.append(lambda pl=pl: wa.scatter(self.o, pl.perm, out=self.out))
+        return out
 
     def run(self, timed=False):
         wa, w, torch = self.wa, self.w, self.torch
@@ -185,6 +210,44 @@ def text_attention_rate(st, torch, text_len=256, reps=10):
             "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4)}
 
 
+FLUSH_BYTES = 1 << 30  # at least the 256 MB Infinity Cache plus the 8 x 4 MB of L2, four times over
+
+
+def permute_rate_flushed(st, torch, reps):
+    """The step's permutes with the caches flushed before each launch: a
+    1 GiB scratch buffer is overwritten and a second 1 GiB buffer is read
+    (which writes the first one's dirty lines back and leaves the caches
+    full of unrelated clean lines), then the permute runs between two
+    events on the launch stream.  GB/s of its algorithmic bytes."""
+    n = FLUSH_BYTES // 4
+    fill = torch.empty(n, dtype=torch.float32, device="cuda")
+    other = torch.zeros(n, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    launches = st.permute_launches()
+    ev = []
+    for r in range(reps + 1):
+        for fn in launches:
+            fill.fill_(float(r))
+            torch.sum(other, dim=0, out=sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st.stream)
+            fn()
+            b.record(st.stream)
+            if r > 0:  # the first round is a warm-up
+                ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    del fill, other
+    avg = sum(ms) / len(ms)
+    gbs = st.perm_bytes_data / (avg * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(avg, 4),
+            "bytes_per_launch": st.perm_bytes_data, "launches": len(ms),
+            "kernel": "permute_rows_kernel (gather, transition, scatter)",
+            "flush": f"{FLUSH_BYTES >> 20} MiB overwritten and another {FLUSH_BYTES >> 20} MiB read before each "
+                     "launch"}
+
+
 def measured_traffic(kernel_prefix, workload):
     """HBM bytes per launch (read + write) recorded in profiles/hbm_traffic.txt
     for a kernel, or None when there is no record for this workload or the
@@ -241,54 +304,80 @@ def practical_ceilings(torch, w, reps=20):
             "copy_gbps": round(copy_gbs, 1), "copy": f"device copy of {x.numel() * 2} bytes"}
 
 
-def cpu_baseline(w, seconds):
-    """The oracle as it stands, timed on the host cores on a bounded sample
-    of the same workload: per-window fp64 attention over the first windows of
-    the first layer's layout, head by head, until the time budget is used."""
+def host_cpu_model():
+    """The host's CPU model name as lscpu reports it (None if unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True,
+                             timeout=10).stdout
+    except Exception:
+        return None
+    for line in out.splitlines():
+        if line.lower().startswith("model name"):
+            return line.split(":", 1)[1].strip()
+    return None
+
+
+def cpu_baseline(st, seconds):
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same workload, on the workload's own bf16 bytes (copied from the
+    device, decoded exactly with the oracle's bf16 decoder): the planner on
+    the whole grid (single-threaded Python), the gather of the whole Q into
+    the first layout (a NumPy take of bf16 bit patterns), and fp64
+    per-window attention over the first layout's windows, head by head,
+    until the time budget is used.  `value` is the attention rate."""
     import numpy as np
     from oracle import attention as oatt
     from oracle import permute as operm
     from oracle import plan as oplan
+    from window_attention_amd.inputs import bf16_bits
+    w = st.w
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
-                      default=1)
+                      default=None)
     except Exception:
-        threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
+        threads = None
+    ncpu = os.cpu_count() or 1
+    threads = threads or ncpu
     method = 0 if w.schedule[0] == "R" else 1
+    t0 = time.perf_counter()
     p = oplan.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, method)
     t_plan = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
+    # the workload's canonical bf16 bytes, [B, L, heads, D] as uint16 bit patterns
+    hq, hk, hv = (bf16_bits(x) for x in (st.q, st.k, st.v))
+    t0 = time.perf_counter()
+    qw = operm.gather(hq, p.perm)
+    t_gather = time.perf_counter() - t0
+    kw, vw = operm.gather(hk, p.perm), operm.gather(hv, p.perm)
+    gather_gbs = 2 * qw.nbytes / t_gather / 1e9
     D = w.head_dim
-    flops = 0
-    done = 0
-    t0 = time.perf_counter()
     scale = 1.0 / math.sqrt(D)
+    flops, done, t_attn = 0, 0, 0.0
     for i in range(p.num_windows):
-        n = p.cu_seqlens[i + 1] - p.cu_seqlens[i]
-        q, k, v = (rng.standard_normal((n, D)) for _ in range(3))
+        a, e = p.cu_seqlens[i], p.cu_seqlens[i + 1]
         for h in range(w.heads):
-            oatt.head_attention(q, k, v, scale)
-            flops += 4 * n * n * D
+            x = [oatt.bf16_bits_to_float64(t[0, a:e, h]) for t in (qw, kw, vw)]
+            t0 = time.perf_counter()
+            oatt.head_attention(x[0], x[1], x[2], scale)
+            t_attn += time.perf_counter() - t0
+            flops += 4 * (e - a) ** 2 * D
             done += 1
-            if time.perf_counter() - t0 > seconds:
+            if t_attn > seconds:
                 break
-        if time.perf_counter() - t0 > seconds:
+        if t_attn > seconds:
             break
-    t_attn = time.perf_counter() - t0
-    # permute sample: gather of 4096 canonical rows of the workload's row size
-    rows = min(4096, w.L)
-    x = rng.integers(0, 2 ** 16, size=(1, w.L, w.heads * D), dtype=np.uint16)
-    t0 = time.perf_counter()
-    operm.gather(x, p.perm[:rows])
-    t_perm = time.perf_counter() - t0
+    lay = "regular" if method == 0 else "shifted"
     return {
         "value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"fp64 window attention of {done} (window, head) pairs of the {w.name} "
-                  f"{'regular' if method == 0 else 'shifted'} layout ({flops / 1e9:.1f} GFLOP in {t_attn:.1f} s); "
-                  f"planner {t_plan:.2f} s for the whole grid; gather {2 * rows * w.heads * D * 2 / t_perm / 1e9:.2f} "
-                  f"GB/s on {rows} rows",
+        "sample": f"fp64 attention (oracle head_attention) of the first {done} (window, head) pairs of the "
+                  f"{w.name} {lay} layout on the workload's own bf16 inputs ({flops / 1e9:.1f} GFLOP in "
+                  f"{t_attn:.1f} s); planner {t_plan:.3f} s for the whole grid; gather of the whole Q "
+                  f"({qw.nbytes / 1e6:.0f} MB) at {gather_gbs:.2f} GB/s",
+        "attention_tflops": round(flops / t_attn / 1e12, 4),
+        "planner_s": round(t_plan, 4),
+        "gather_gbps": round(gather_gbs, 3),
+        "host": {"cpu_count": ncpu, "blas_threads": threads, "model": host_cpu_model()},
     }
 
 
@@ -347,15 +436,20 @@ def main():
     nl = len(w.schedule)
     attn_flops_step = sum(st.attn_flops)
     attn_ms_step = sum(attn_ms) / args.steps
-    perm_ms_step = sum(perm_ms) / args.steps
     attn_tfs = attn_flops_step / (attn_ms_step * 1e-3) / 1e12
     perm_bytes_launch = st.perm_bytes_data
     perm_gbs = perm_bytes_launch / (sum(perm_ms) / len(perm_ms) * 1e-3) / 1e9
+    layers = []
     for li, lay in enumerate(w.schedule):
         ms = sorted(attn_ms[li::nl])[len(attn_ms[li::nl]) // 2]
+        layers.append({"layout": lay, "median_ms": round(ms, 4),
+                       "tflops": round(st.attn_flops[li] / ms / 1e9, 2)})
         log(f"[bench] attn layer {li} ({lay}): median {ms:.3f} ms, {st.attn_flops[li] / ms / 1e9:.1f} TFLOP/s")
-    log(f"[bench] permutes: {len(perm_ms) // args.steps}/step, mean {sum(perm_ms) / len(perm_ms) * 1e3:.1f} us, "
-        f"{perm_gbs:.0f} GB/s")
+    log(f"[bench] permutes in the step: {len(perm_ms) // args.steps}/step, mean "
+        f"{sum(perm_ms) / len(perm_ms) * 1e3:.1f} us, {perm_gbs:.0f} GB/s")
+    flushed = permute_rate_flushed(st, torch, args.steps)
+    log(f"[bench] permutes after a cache flush: mean {flushed['avg_launch_ms'] * 1e3:.1f} us, "
+        f"{flushed['achieved']:.0f} GB/s")
     value = attn_flops_step / (ms_step * 1e-3) / 1e12
     rope = rope_gather_rate(st, torch)
     if rope:
@@ -365,13 +459,34 @@ def main():
         t = measured_traffic("rope_rows_kernel", w.name)
         rope["traffic"], rope["traffic_detail"] = (t["total_bytes"] if t else None), t
     if text:
-        t = measured_traffic("attn_fwd_kernel<128,4,1,true>", w.name)
+        t = measured_traffic(ATTN_KERNEL + "true>", w.name)
         m = measured_traffic("text_mean_kernel", w.name)
         text["traffic"] = t["total_bytes"] + m["total_bytes"] if t and m else None
         text["traffic_detail"] = {"attn_fwd_kernel": t, "text_mean_kernel": m} if t and m else None
         log(f"[bench] text attention (beside the step): {text['avg_call_ms']:.3f} ms, {text['achieved']:.0f} TFLOP/s")
-    attn_traffic = measured_traffic("attn_fwd_kernel<128,4,1,false>", w.name)
+    attn_traffic = measured_traffic(ATTN_KERNEL + "false>", w.name)
     perm_traffic = measured_traffic("permute_rows_kernel<transition>", w.name)
+    # Roofline of the attention kernel.  Its algorithmic HBM bytes per launch
+    # are one read of Q, K, V and one write of O; below the ridge point
+    # (peak flops / peak bandwidth, 312.5 flop/B) the kernel is HBM-bound and
+    # its ceiling is the bytes at 8 TB/s.
+    attn_bytes = 4 * w.batch * w.L * w.heads * w.head_dim * 2
+    flops_launch = attn_flops_step / nl
+    intensity = flops_launch / attn_bytes
+    ceiling_tfs = min(BF16_MFMA_PEAK_TFS, intensity * HBM_PEAK_GBS / 1e3)
+    launch_ms = attn_ms_step / nl
+    if intensity < BF16_MFMA_PEAK_TFS * 1e3 / HBM_PEAK_GBS:
+        gbs = attn_bytes / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(attn_tfs, 2), "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(attn_tfs / BF16_MFMA_PEAK_TFS, 4)}
+    roof.update({"traffic": attn_traffic["total_bytes"] if attn_traffic else None,
+                 "traffic_detail": attn_traffic, "kernel": "attn_fwd_kernel", "avg_launch_ms": round(launch_ms, 4),
+                 "flops_per_launch": flops_launch, "bytes_per_launch": attn_bytes,
+                 "flop_per_byte": round(intensity, 1), "ceiling_tflops": round(ceiling_tfs, 1),
+                 "frac_of_ceiling": round(attn_tfs / ceiling_tfs, 4), "layers": layers})
     res = {
         "metric": "window-attn useful TFLOP/s + permute GB/s, 21x45x80 grid bf16, 1 GPU",
         "value": round(value, 2),
@@ -389,21 +504,16 @@ def main():
                    "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "entry": w.entry,
                    "schedule": ",".join(w.schedule), "parallelism": "none (1 GPU)"},
         "attn_tflops": round(attn_tfs, 2),
-        "permute_gbps": round(perm_gbs, 1),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tfs, 2), "peak": BF16_MFMA_PEAK_TFS,
-                     "unit": "TFLOP/s", "frac": round(attn_tfs / BF16_MFMA_PEAK_TFS, 4),
-                     "traffic": attn_traffic["total_bytes"] if attn_traffic else None,
-                     "traffic_detail": attn_traffic,
-                     "kernel": "attn_fwd_kernel",
-                     "avg_launch_ms": round(attn_ms_step / nl, 4),
-                     "flops_per_launch": attn_flops_step / nl},
-        "roofline_permute": {"bound": "hbm", "achieved": round(perm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(perm_gbs / HBM_PEAK_GBS, 4),
-                             "traffic": perm_traffic["total_bytes"] if perm_traffic else None,
-                             "traffic_detail": perm_traffic,
-                             "kernel": "permute_rows_kernel (gather, transition, scatter)",
-                             "avg_launch_ms": round(sum(perm_ms) / len(perm_ms), 4),
-                             "bytes_per_launch": perm_bytes_launch},
+        "permute_gbps": round(flushed["achieved"], 1),
+        "roofline": roof,
+        "roofline_permute": dict(flushed, traffic=perm_traffic["total_bytes"] if perm_traffic else None,
+                                 traffic_detail=perm_traffic),
+        "roofline_permute_in_step": {"bound": "hbm", "achieved": round(perm_gbs, 1), "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": round(perm_gbs / HBM_PEAK_GBS, 4),
+                                     "kernel": "permute_rows_kernel (gather, transition, scatter)",
+                                     "avg_launch_ms": round(sum(perm_ms) / len(perm_ms), 4),
+                                     "bytes_per_launch": perm_bytes_launch,
+                                     "note": "timed inside the step, caches as the step leaves them"},
         "roofline_rope_permute": rope,
         "roofline_text_attention": text,
     }
@@ -417,7 +527,7 @@ def main():
         res["practical_ceilings"] = ceil
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle sample, about {args.cpu_seconds:.0f} s")
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(st, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -160,7 +160,10 @@ int win_transition(const void* src, void* dst, const int32_t* inv_src, const int
  *              these rules are clamped so that no access leaves the tensors;
  *              the rows involved are then unspecified.  Rows outside every
  *              window are not written.
- * head_dim     64 or 128.  softmax_scale > 0 (1/sqrt(head_dim) is the usual).
+ * head_dim     64 or 128.
+ * softmax_scale > 0, or 0 for the default 1/sqrt(head_dim) (the scaled
+ *              dot-product convention; computed in double, rounded to float);
+ *              negative, NaN or infinite values are WIN_EINVAL.
  * Arithmetic: bf16 inputs, fp32 MFMA accumulation and fp32 online softmax,
  * bf16 output rounded to nearest even.  Deterministic: no atomics, a fixed
  * reduction order per output row, independent of batch size and grid.

@@ -15,22 +15,37 @@ from window_attention_amd.inputs import bf16_bits
 # tolerance of bf16-in / fp32-accumulate attention against the fp64 oracle
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
-# LSE bound per query row.  The kernel's scores are fp32 sums of exact bf16
-# products and its normaliser is the fp32 sum of fp32 probabilities, so its
-# LSE error is at the fp32 level; the bound is deliberately looser:
-#  * 2^-9 for a normaliser summed from bf16-rounded probabilities;
-#  * 2^-9 * scale * sum_d |q_d k_d| for a score computed from operands
-#    rounded once more to bf16 (a log-sum-exp moves by at most the largest
-#    such change over the keys) -- the kernel rounds none, and a kernel that
-#    folded the softmax scale into a bf16 Q would fail it on peaked rows;
-#  * 5e-4 for exp2 / log and the fp32 accumulations.
-LSE_SLACK = 5e-4
+# LSE bound per query row, from the kernel's arithmetic (no bf16 rounding
+# touches the LSE: the bf16 probabilities only feed the P V product).
+# LSE = log sum_k exp(x_k) with x_k = scale * s_k moves by at most
+# max_k |dx_k| (its gradient is the softmax row), so the bound is:
+#  * scores: s_k is an fp32 sum of D exact bf16 products, at most D
+#    roundings of 2^-23 relative to sum_d |q_d k_d| (truncation covered);
+#    c = scale * log2(e) and the caller's scale are fp32, 2^-22 relative
+#    to |x_k| in all; the fma c * s - ref rounds once, relative to a result
+#    of at most ~2^5 for any key that contributes (2^-18);
+#  * normaliser: fp32 exp2 per probability (2^-21 relative), row sums of
+#    positive terms added in chains of at most 32 + tiles + 2 roundings, and
+#    one exp2 factor (2^-21) and one product (2^-24) per reference move, at
+#    most one move per 64-key tile; a relative error e of the sum is e in
+#    the log;
+#  * the final fp32 combination ref * ln 2 + log(sum): 2^-21 relative to
+#    the magnitudes involved, at most max_k |x_k| + log(n) + 8 * ln 2
+#    (probabilities stay below 2^8 against the reference).
+KEY_TILE = 64
 
 
 def lse_bound(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
-    """Per-row LSE tolerance for one window and head: q, k are [n, D]."""
-    worst = (np.abs(q) @ np.abs(k).T).max(axis=1)
-    return 2.0 ** -9 + 2.0 ** -9 * scale * worst + LSE_SLACK
+    """Per-row LSE tolerance for one segment and head: q [n, D] queries,
+    k [m, D] the keys they attend to (fp64 copies of the bf16 inputs)."""
+    D = q.shape[1]
+    m = k.shape[0]
+    s_abs = np.abs(q @ k.T) * scale
+    score = (D * 2.0 ** -23 * scale * (np.abs(q) @ np.abs(k).T) + 2.0 ** -22 * s_abs).max(axis=1) + 2.0 ** -18
+    tiles = math.ceil(m / KEY_TILE) + 1  # text keys start on a tile of their own
+    norm = 2.0 ** -21 + (32 + tiles + 2) * 2.0 ** -24 + tiles * (2.0 ** -21 + 2.0 ** -24)
+    final = 2.0 ** -21 * (s_abs.max(axis=1) + math.log(max(m, 1)) + 8 * math.log(2.0))
+    return score + norm + final
 
 
 def lse_bound_windows(q, k, cu, scale=None):

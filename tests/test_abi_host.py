@@ -138,7 +138,10 @@ def test_device_entry_points_validate_before_launch():
     assert lib.win_attn_fwd(None, A, B, O, None, I, 1, 8, 8, 1, 1, 128, f(0.1), None) == -1
     assert lib.win_attn_fwd(A, A, A, O, None, None, 1, 8, 8, 1, 1, 128, f(0.1), None) == -1
     assert lib.win_attn_fwd(A, A, A, O, None, I, 1, 8, 8, 1, 1, 96, f(0.1), None) == -2   # head_dim
-    assert lib.win_attn_fwd(A, A, A, O, None, I, 1, 8, 8, 1, 1, 128, f(0.0), None) == -1  # scale
+    assert lib.win_attn_fwd(A, A, A, O, None, I, 1, 8, 8, 1, 1, 128, f(-0.1), None) == -1  # scale
+    assert lib.win_attn_fwd(A, A, A, O, None, I, 1, 8, 8, 1, 1, 128, f(float("inf")), None) == -1
+    # 0 selects the default scale; the call still fails on the head_dim
+    assert lib.win_attn_fwd(A, A, A, O, None, I, 1, 8, 8, 1, 1, 96, f(0.0), None) == -2
     assert lib.win_attn_fwd(A, A, A, O, None, I, 1, 8, 8, 1, 1, 128, f(float("nan")), None) == -1
     assert lib.win_attn_fwd(M, A, A, O, None, I, 1, 8, 8, 1, 1, 128, f(0.1), None) == -2
     assert lib.win_attn_fwd(A, B, C, A, None, I, 1, 8, 8, 1, 1, 128, f(0.1), None) == -1  # o aliases q
@@ -150,3 +153,20 @@ def test_device_entry_points_validate_before_launch():
     Q2, K2, V2, O2 = (ctypes.c_void_p(i << 40) for i in (1, 2, 3, 4))
     assert lib.win_attn_fwd(Q2, K2, V2, O2, None, I, 1, 8, 8, 1, 1 << 17, 128, f(0.1), None) == -3
     assert lib.win_attn_fwd(Q2, K2, V2, O2, None, I, 0, 8, 8, 1, (1 << 17) - 1, 128, f(0.1), None) == 0
+
+
+@pytest.mark.parametrize("grid", [(1, 1, 20000), (3, 1, 15000), (2, 20000, 1)])
+def test_plan_rejects_zero_rescaled_extent(grid):
+    """rh or rw rounds to 0 (1x20000 gives H * scale = 0.42): WIN_EINVAL for
+    the size query and the host and device fills, nothing written."""
+    lib = wa.load_library()
+    info = wa._PlanInfo()
+    assert lib.win_plan(*grid, 1, 1, 1, 0, ctypes.byref(info), None, None, None, None, 0, None) == -1
+    L = grid[0] * grid[1] * grid[2]
+    perm = np.full(L, -7, dtype=np.int32)
+    assert lib.win_plan(*grid, 1, 1, 1, 1, ctypes.byref(info), perm.ctypes.data, None, None, None, 0, None) == -1
+    assert np.all(perm == -7)
+    # device fill: rejected before anything is enqueued (the pointer is never touched)
+    assert lib.win_plan(*grid, 1, 1, 1, 0, ctypes.byref(info), ctypes.c_void_p(0x10000), None, None, None, 1,
+                        None) == -1
+

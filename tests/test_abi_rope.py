@@ -4,6 +4,7 @@ import ctypes
 import math
 
 import numpy as np
+import torch
 import pytest
 
 import window_attention_amd as wa
@@ -104,3 +105,31 @@ def test_errors():
     assert f(A, B, I, None, None, I, 6, 15, 27, 8, 1, 1, 128, 126, None) == -1        # local missing
     assert f(A, B, I, None, I, ctypes.c_void_p(0x2000004), 6, 15, 27, 8, 1, 1, 128, 126, None) == -2  # table alignment
     assert f(None, None, None, None, None, None, 6, 15, 27, 0, 1, 1, 128, 126, None) == 0  # empty
+
+
+@pytest.mark.parametrize("what", ["idx", "perm_dst", "local", "table", "rope_dim"])
+def test_binding_rejects_tables_of_another_size(what):
+    """The binding checks every table against the source before calling the
+    library, whose kernel reads them through raw pointers: an index table,
+    local table or rotation table of another grid, layout or rope_dim is
+    refused (checked first, so host tensors show it without a GPU)."""
+    p = wa.plan(5, 9, 16, 2, 3, 3, wa.SHIFTED)
+    L = p.num_tokens
+    src = torch.zeros((1, L, 2, 128), dtype=torch.bfloat16)
+    idx, perm_dst = torch.zeros(L, dtype=torch.int32), torch.zeros(L, dtype=torch.int32)
+    local = torch.zeros(3 * L, dtype=torch.int32)
+    rope_dim = 126
+    table = torch.zeros((p.wt + p.wh + p.ww) * (rope_dim // 3), dtype=torch.float32)
+    if what == "idx":
+        idx = idx[:-1]
+    elif what == "perm_dst":
+        perm_dst = torch.zeros(L + 1, dtype=torch.int32)
+    elif what == "local":
+        local = local[:-3]
+    elif what == "table":
+        table = torch.zeros(table.numel() - 2, dtype=torch.float32)
+    else:
+        rope_dim = 120  # a table made for 126 channels
+    with pytest.raises(wa.WinAttnError) as e:
+        wa._permute_rope(src, idx, perm_dst, local, table, p, rope_dim, None)
+    assert "must be a device tensor" not in str(e.value)

@@ -145,7 +145,8 @@ def test_closed_forms_on_device():
         mean = vh[:, a:e].mean(axis=1, keepdims=True)
         assert np.max(np.abs(to_f64(o[:, a:e]) - mean)) <= MAX_ABS
         # q = 0: every score is 0 exactly, so only the normaliser's rounding is left
-        assert np.max(np.abs(lse[:, :, a:e].cpu().numpy() - math.log(n))) <= 2.0 ** -9 + 5e-4
+        bound = lse_bound(np.zeros((n, D)), to_f64(k[0, a:e, 0]), 1.0 / math.sqrt(D))
+        assert np.all(np.abs(lse[:, :, a:e].double().cpu().numpy() - math.log(n)) <= bound)
 
 
 @pytest.mark.parametrize("method", [0, 1])
@@ -286,3 +287,15 @@ def test_argument_errors():
     q = torch.zeros((1, 8, 1, 128), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(wa.WinAttnError):
         wa.attn_fwd(q, q, q, cu, 8, out=q)     # output aliases the inputs
+
+
+def test_default_scale_sentinel():
+    """softmax_scale None passes 0, which the library turns into
+    1/sqrt(head_dim): bit-identical to passing that value."""
+    lengths = [130, 64, 7]
+    cu = torch.as_tensor(_cu(lengths), device=DEV)
+    for D in (64, 128):
+        q, k, v = (normal((1, sum(lengths), 2, D), 540 + t, device=DEV) for t in range(3))
+        o0, l0 = wa.attn_fwd(q, k, v, cu, max(lengths), return_lse=True)
+        o1, l1 = wa.attn_fwd(q, k, v, cu, max(lengths), softmax_scale=1.0 / math.sqrt(D), return_lse=True)
+        assert torch.equal(o0, o1) and torch.equal(l0, l1)

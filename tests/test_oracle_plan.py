@@ -71,3 +71,11 @@ def test_rejects_non_positive(bad):
 def test_rejects_unknown_method():
     with pytest.raises(ValueError):
         oplan.plan(2, 3, 4, 1, 1, 1, 7)
+
+
+@pytest.mark.parametrize("grid", [(1, 1, 20000), (3, 1, 15000), (2, 20000, 1)])
+def test_zero_rescaled_extent_is_rejected(grid):
+    """A rescaled extent of zero (1x20000: H * sqrt(3600 / 20000) = 0.42
+    rounds to 0) gives no window size: the planner refuses the grid."""
+    with pytest.raises(ValueError):
+        oplan.window_size(*grid, 1, 1, 1)

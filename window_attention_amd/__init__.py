@@ -331,15 +331,27 @@ def rope_table(p: Plan, text_len, rope_dim, base=10000.0, device=None):
 def _permute_rope(src, idx, perm_dst, local, table, p: Plan, rope_dim, out):
     import torch
     lib = load_library()
+    if src.dim() != 4:
+        raise WinAttnError(-1, "src must be [B, L, heads, head_dim]")
+    B, L, Hh, D = src.shape
+    # the kernel reads these tables through raw pointers: sizes from another
+    # grid, layout or rope_dim would send it past their ends (checked before
+    # anything else, so a mismatch is reported whatever the devices)
+    if idx.numel() != L or (perm_dst is not None and perm_dst.numel() != L):
+        raise WinAttnError(-1, f"index tables must have L={L} entries")
+    if local.numel() != 3 * L:
+        raise WinAttnError(-1, f"local must have 3*L={3 * L} entries, got {local.numel()}")
+    if rope_dim < 6 or rope_dim > D or (rope_dim // 3) % 2:
+        raise WinAttnError(-2, f"rope_dim {rope_dim} is not supported for head_dim {D}")
+    want = (p.wt + p.wh + p.ww) * (rope_dim // 3)
+    if table.numel() != want:
+        raise WinAttnError(-1, f"table must hold (wt+wh+ww)*(rope_dim//3)={want} floats, got {table.numel()}")
     _require_cuda("src", src, torch.bfloat16)
     for name, t in (("idx", idx), ("local", local)):
         _require_cuda(name, t, torch.int32)
     if perm_dst is not None:
         _require_cuda("perm_dst", perm_dst, torch.int32)
     _require_cuda("table", table, torch.float32)
-    if src.dim() != 4:
-        raise WinAttnError(-1, "src must be [B, L, heads, head_dim]")
-    B, L, Hh, D = src.shape
     if out is None:
         out = torch.empty_like(src)
     _require_cuda("out", out, torch.bfloat16)
@@ -419,8 +431,9 @@ def transition(src, inv_src, perm_dst, out=None):
 
 def attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, out=None, return_lse=False):
     """Window attention over window-ordered bf16 ``[B, L, heads, head_dim]``
-    tensors; windows are the ``cu_seqlens`` segments.  Returns ``out`` or
-    ``(out, lse)`` with ``lse`` fp32 ``[B, heads, L]``."""
+    tensors; windows are the ``cu_seqlens`` segments.  ``softmax_scale`` None
+    passes 0, the library's sentinel for ``1/sqrt(head_dim)``.  Returns ``out``
+    or ``(out, lse)`` with ``lse`` fp32 ``[B, heads, L]``."""
     import torch
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -430,7 +443,7 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, out=None, retu
     _require_cuda("cu_seqlens", cu_seqlens, torch.int32)
     B, L, Hh, D = q.shape
     if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(D)
+        softmax_scale = 0.0  # the library's default, 1/sqrt(head_dim)
     if out is None:
         out = torch.empty_like(q)
     _require_cuda("out", out, torch.bfloat16)
@@ -464,7 +477,7 @@ def attn_fwd_text(q, k, v, cu_seqlens, max_seqlen, text_q, text_k, text_v, softm
     T = text_q.shape[1]
     N = cu_seqlens.numel() - 1
     if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(D)
+        softmax_scale = 0.0  # the library's default, 1/sqrt(head_dim)
     if out is None:
         out = torch.empty_like(q)
     if text_out is None:
@@ -481,3 +494,4 @@ def attn_fwd_text(q, k, v, cu_seqlens, max_seqlen, text_q, text_k, text_v, softm
                                  int(max_seqlen), L, B, Hh, D, float(softmax_scale), _ptr(text_q), _ptr(text_k),
                                  _ptr(text_v), T, _ptr(text_out), _ptr(workspace), _stream(q)), "win_attn_fwd_text")
     return (out, text_out, lse) if return_lse else (out, text_out)
+

@@ -930,8 +930,10 @@ int attn_impl(const void* q, const void* k, const void* v, void* o, float* lse, 
               float* text_partial, void* stream) {
     if (!q || !k || !v || !o || !cu_seqlens) return WIN_EINVAL;
     if (num_windows < 0 || max_seqlen < 0 || L < 0 || batch <= 0 || heads <= 0 || text_len < 0) return WIN_EINVAL;
-    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return WIN_EINVAL;
     if (head_dim != 64 && head_dim != 128) return WIN_EUNSUPPORTED;
+    // 0 selects the scaled-dot-product default 1/sqrt(head_dim)
+    if (softmax_scale == 0.f) softmax_scale = (float)(1.0 / std::sqrt((double)head_dim));
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return WIN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return WIN_EUNSUPPORTED;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return WIN_EUNSUPPORTED;
     if (L >= ((int64_t)1 << 31) || max_seqlen > L) return max_seqlen > L ? WIN_EINVAL : WIN_EOVERFLOW;

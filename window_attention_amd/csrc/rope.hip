@@ -67,8 +67,8 @@ struct RopeArgs {
 // lane picks the one of its pairs' axis.
 __device__ __forceinline__ void row_rotation(const RopeArgs& a, int32_t j, uint32_t lane, f32x2 (&cs)[4],
                                              bool (&rot)[4]) {
-    const int32_t loc[3] = {clamp_to(a.local[3 * j], a.ext[0]), clamp_to(a.local[3 * j + 1], a.ext[1]),
-                            clamp_to(a.local[3 * j + 2], a.ext[2])};
+    const int32_t* lj = a.local + 3 * (int64_t)j;  // 3 j passes 2^31 before j does
+    const int32_t loc[3] = {clamp_to(lj[0], a.ext[0]), clamp_to(lj[1], a.ext[1]), clamp_to(lj[2], a.ext[2])};
     const int32_t cb = (int32_t)lane % a.head_chunks;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
