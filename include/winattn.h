@@ -63,6 +63,7 @@ extern "C" {
 #define WIN_EUNSUPPORTED (-2) /* dtype, head_dim, row size or alignment not handled */
 #define WIN_EOVERFLOW    (-3) /* a size or index exceeds the 32-bit index range */
 #define WIN_EDEVICE      (-4) /* the HIP runtime reported an error */
+#define WIN_ESCRATCH     (-5) /* the work needs more than the library's static scratch */
 
 /* ---- enumerations -------------------------------------------------------- */
 #define WIN_METHOD_REGULAR 0 /* slice(k*w, min((k+1)*w, n)) on every axis */
@@ -334,6 +335,31 @@ int win_attn_fwd_text(const void* q, const void* k, const void* v, void* o, floa
                       int32_t num_windows, int32_t max_seqlen, int64_t L, int32_t batch, int32_t heads,
                       int32_t head_dim, float softmax_scale, const void* text_q, const void* text_k,
                       const void* text_v, int32_t text_len, void* text_o, float* text_partial, void* stream);
+
+/*
+ * win_attn_fwd_text without the caller's workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation, harnesses without an allocator): the per-window text
+ * outputs go to a static device array of WIN_TEXT_SCRATCH_BYTES bytes that
+ * the library holds on each device it runs on until the process ends.  The
+ * caller passes inputs and outputs as for win_attn_fwd_text; nothing is
+ * allocated or freed by the call.
+ *   batch * num_windows * text_len * heads * head_dim * 4 bytes must fit the
+ *   array: WIN_ESCRATCH otherwise (nothing enqueued).  With 24 heads x 128
+ *   that is, e.g., 256 text rows on 21 windows or 85 rows on 64 windows.
+ * Every call on one device uses that device's one array: calls that overlap
+ * on one device (two streams, or two host threads) race and their outputs
+ * are unspecified; calls ordered on one stream do not.  Each call writes
+ * every slot it reads, so no clearing is needed between calls.
+ * Results are bit-identical to win_attn_fwd_text.  Errors: as
+ * win_attn_fwd_text, plus WIN_ESCRATCH.
+ */
+#define WIN_TEXT_SCRATCH_BYTES ((int64_t)64 << 20)
+int win_attn_fwd_text_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int32_t* cu_seqlens, int32_t num_windows, int32_t max_seqlen, int64_t L,
+                              int32_t batch, int32_t heads, int32_t head_dim, float softmax_scale,
+                              const void* text_q, const void* text_k, const void* text_v, int32_t text_len,
+                              void* text_o, void* stream);
 
 /* Static string naming a status code. */
 const char* win_strerror(int status);

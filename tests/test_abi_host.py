@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_build_info():
     lib = wa.load_library()
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert lib.win_strerror(code).decode() != "unknown status"
     assert lib.win_strerror(-99).decode() == "unknown status"
     assert "gfx950" in wa.build_info()
@@ -170,3 +170,15 @@ def test_plan_rejects_zero_rescaled_extent(grid):
     assert lib.win_plan(*grid, 1, 1, 1, 0, ctypes.byref(info), ctypes.c_void_p(0x10000), None, None, None, 1,
                         None) == -1
 
+
+def test_noalloc_text_attention_refuses_work_past_its_scratch():
+    """win_attn_fwd_text_noalloc checks the size of its per-window text
+    outputs against the static scratch before anything else touches the
+    device (fake pointers: never dereferenced)."""
+    lib = wa.load_library()
+    f = ctypes.c_float
+    Q, K, V, O, I, TQ, TK, TV, TO = (ctypes.c_void_p(i << 32) for i in range(1, 10))
+    args = lambda N, T, B=1, H=24: (Q, K, V, O, None, I, N, 8, 8, B, H, 128, f(0.0), TQ, TK, TV, T, TO, None)  # noqa
+    for N, T, B, H in ((8, 683, 1, 24), (64, 86, 1, 24), (1 << 30, 1 << 30, 1 << 30, 1 << 30)):
+        assert lib.win_attn_fwd_text_noalloc(*args(N, T, B, H)) == -5
+    assert "scratch" in lib.win_strerror(-5).decode()

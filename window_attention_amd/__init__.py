@@ -11,6 +11,7 @@ memory and the current stream.  The C entry points are documented in
     transition()  -> win_transition
     attn_fwd()    -> win_attn_fwd
     attn_fwd_text() -> win_attn_fwd_text
+    attn_fwd_text_noalloc() -> win_attn_fwd_text_noalloc
     pack()        -> win_pack
     lpt()         -> win_lpt
     local_positions() -> win_plan_local
@@ -31,7 +32,7 @@ from dataclasses import dataclass
 
 __all__ = ["WinAttnError", "Plan", "Packed", "Assignment", "Redistribution", "plan", "plan_cached", "pack", "lpt",
            "plan_a", "local_positions", "rope_table", "gather_rope", "transition_rope", "gather", "scatter",
-           "transition", "attn_fwd", "attn_fwd_text", "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
+           "transition", "attn_fwd", "attn_fwd_text", "attn_fwd_text_noalloc", "build_info", "REGULAR", "SHIFTED", "LIB_PATH"]
 
 REGULAR = 0
 SHIFTED = 1
@@ -89,6 +90,9 @@ def load_library():
     lib.win_attn_fwd_text.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, vp, vp, vp, i32,
                                       vp, vp, vp]
     lib.win_attn_fwd_text.restype = ctypes.c_int
+    lib.win_attn_fwd_text_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, vp, vp, vp,
+                                              i32, vp, vp]
+    lib.win_attn_fwd_text_noalloc.restype = ctypes.c_int
     lib.win_strerror.argtypes = [ctypes.c_int]
     lib.win_strerror.restype = ctypes.c_char_p
     lib.win_build_info.argtypes = []
@@ -495,3 +499,41 @@ def attn_fwd_text(q, k, v, cu_seqlens, max_seqlen, text_q, text_k, text_v, softm
                                  _ptr(text_v), T, _ptr(text_out), _ptr(workspace), _stream(q)), "win_attn_fwd_text")
     return (out, text_out, lse) if return_lse else (out, text_out)
 
+
+def attn_fwd_text_noalloc(q, k, v, cu_seqlens, max_seqlen, text_q, text_k, text_v, softmax_scale=None, out=None,
+                          text_out=None, lse=None):
+    """``attn_fwd_text`` whose per-window text outputs live in the library's
+    static device scratch instead of a caller workspace (see
+    ``win_attn_fwd_text_noalloc``).  ``out``, ``text_out`` and the optional
+    fp32 ``lse`` [B, heads, L] are the caller's; pass them all for a call that
+    allocates nothing.  Returns ``(out, text_out)``."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require_cuda(name, t, torch.bfloat16)
+        if t.dim() != 4 or t.shape != q.shape:
+            raise WinAttnError(-1, f"{name} must be [B, L, heads, head_dim] like q")
+    B, L, Hh, D = q.shape
+    for name, t in (("text_q", text_q), ("text_k", text_k), ("text_v", text_v)):
+        _require_cuda(name, t, torch.bfloat16)
+        if t.dim() != 4 or t.shape != text_q.shape or t.shape[0] != B or t.shape[2:] != q.shape[2:]:
+            raise WinAttnError(-1, f"{name} must be [B, text_len, heads, head_dim] like text_q")
+    _require_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    if text_out is None:
+        text_out = torch.empty_like(text_q)
+    _require_cuda("out", out, torch.bfloat16)
+    _require_cuda("text_out", text_out, torch.bfloat16)
+    if out.shape != q.shape or text_out.shape != text_q.shape:
+        raise WinAttnError(-1, "out or text_out has the wrong shape")
+    if lse is not None:
+        _require_cuda("lse", lse, torch.float32)
+        if lse.shape != (B, Hh, L):
+            raise WinAttnError(-1, "lse must be [B, heads, L]")
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(lib.win_attn_fwd_text_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+                                         cu_seqlens.numel() - 1, int(max_seqlen), L, B, Hh, D, scale, _ptr(text_q),
+                                         _ptr(text_k), _ptr(text_v), text_q.shape[1], _ptr(text_out), _stream(q)),
+           "win_attn_fwd_text_noalloc")
+    return out, text_out

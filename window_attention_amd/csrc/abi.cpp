@@ -13,6 +13,8 @@ extern "C" const char* win_strerror(int status) {
             return "size or index exceeds the 32-bit index range";
         case WIN_EDEVICE:
             return "HIP runtime error";
+        case WIN_ESCRATCH:
+            return "the work needs more than the library's static scratch (WIN_TEXT_SCRATCH_BYTES)";
         default:
             return "unknown status";
     }

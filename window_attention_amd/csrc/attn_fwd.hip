@@ -52,6 +52,7 @@
 //     and value rows past it fail the copies' buffer range check and are
 //     masked to -inf as keys, so no access leaves the window's rows.
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 
@@ -999,6 +1000,34 @@ int attn_impl(const void* q, const void* k, const void* v, void* o, float* lse, 
 
 }  // namespace
 
+// Per-window text outputs of win_attn_fwd_text_noalloc: a static device array
+// (each device holds its own copy from module load until the process ends).
+// Host code never names it as an address: the device address comes from
+// hipGetSymbolAddress, once per device with that device current.
+static __device__ __align__(256) float scratch[WIN_TEXT_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WIN_EDEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return WIN_EDEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return WIN_OK;
+}
+
+}  // namespace
+
 extern "C" int win_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                             const int32_t* cu_seqlens, int32_t num_windows, int32_t max_seqlen, int64_t L,
                             int32_t batch, int32_t heads, int32_t head_dim, float softmax_scale, void* stream) {
@@ -1013,4 +1042,28 @@ extern "C" int win_attn_fwd_text(const void* q, const void* k, const void* v, vo
                                  void* text_o, float* text_partial, void* stream) {
     return attn_impl(q, k, v, o, lse, cu_seqlens, num_windows, max_seqlen, L, batch, heads, head_dim, softmax_scale,
                      text_q, text_k, text_v, text_len, text_o, text_partial, stream);
+}
+
+extern "C" int win_attn_fwd_text_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                         const int32_t* cu_seqlens, int32_t num_windows, int32_t max_seqlen,
+                                         int64_t L, int32_t batch, int32_t heads, int32_t head_dim,
+                                         float softmax_scale, const void* text_q, const void* text_k,
+                                         const void* text_v, int32_t text_len, void* text_o, void* stream) {
+    void* ws = nullptr;
+    if (text_len > 0) {
+        if (num_windows < 0 || batch <= 0 || heads <= 0 || head_dim <= 0) return WIN_EINVAL;
+        // the per-window text outputs (batch * num_windows * text_len * heads
+        // rows of head_dim floats) must fit the static array; checked factor
+        // by factor, so no product leaves int64
+        const int64_t limit = WIN_TEXT_SCRATCH_BYTES / 4 / head_dim;
+        int64_t rows = 1;
+        for (const int64_t f : {(int64_t)batch, (int64_t)num_windows, (int64_t)text_len, (int64_t)heads}) {
+            rows *= f;
+            if (rows > limit) return WIN_ESCRATCH;
+        }
+        const int st = scratch_address(&ws);
+        if (st != WIN_OK) return st;
+    }
+    return attn_impl(q, k, v, o, lse, cu_seqlens, num_windows, max_seqlen, L, batch, heads, head_dim, softmax_scale,
+                     text_q, text_k, text_v, text_len, text_o, static_cast<float*>(ws), stream);
 }
