@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the practical-ceiling measurements (vendor GEMM and plain copy)")
+    ap.add_argument("--clock", action="store_true",
+                    help="also sample the shader clock (rocm-smi, read-only) while each attention layer runs in a loop")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain device-to-device copy of one workload tensor (the reference kernel of "
                          "known size for HBM byte counters)")
@@ -304,6 +306,65 @@ def practical_ceilings(torch, w, reps=20):
             "copy_gbps": round(copy_gbs, 1), "copy": f"device copy of {x.numel() * 2} bytes"}
 
 
+def sample_sclk(stop, out):
+    """Shader clock readings (MHz) of `rocm-smi --showclocks` until stop is set."""
+    import subprocess
+    while not stop.is_set():
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                               text=True, timeout=5).stdout
+            for ln in r.splitlines():
+                if "sclk" in ln and "(" in ln and "Mhz" in ln:
+                    out.append(int(ln.split("(")[1].split("Mhz")[0]))
+                    break
+        except Exception:
+            return
+        time.sleep(0.1)
+
+
+def attention_clock(st, torch, seconds=2.0):
+    """Each distinct layout's attention call in a loop for about `seconds`,
+    with the shader clock sampled meanwhile: per layout the median clock, the
+    rate and the useful flops per clock cycle per CU."""
+    import threading
+    wa, w = st.wa, st.w
+    out = {}
+    cur = w.entry
+    src = st.bufs[0]
+    for x, dst in zip((st.q, st.k, st.v), src):
+        wa.gather(x, st.plans[cur].perm, out=dst)
+    for li, lay in enumerate(w.schedule):
+        if lay in out:
+            continue
+        pl = st.plans[lay]
+        if lay != cur:
+            for s_, d_ in zip(src, st.bufs[1]):
+                wa.transition(s_, st.plans[cur].inv, pl.perm, out=d_)
+            src, cur = st.bufs[1], lay
+        call = lambda: wa.attn_fwd(src[0], src[1], src[2], pl.cu_seqlens, pl.max_seqlen, out=st.o)  # noqa: E731
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        clk, stop = [], threading.Event()
+        th = threading.Thread(target=sample_sclk, args=(stop, clk))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(1, int(seconds / 1.5e-3))
+        th.start()
+        a.record(st.stream)
+        for _ in range(n):
+            call()
+        b.record(st.stream)
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        ms = a.elapsed_time(b) / n
+        tfs = st.attn_flops[li] / (ms * 1e-3) / 1e12
+        mhz = sorted(clk)[len(clk) // 2] if clk else None
+        out[lay] = {"ms": round(ms, 4), "tflops": round(tfs, 1), "sclk_mhz": mhz, "samples": len(clk),
+                    "flop_per_cycle_per_cu": round(tfs * 1e12 / (mhz * 1e6) / 256, 1) if mhz else None}
+    return out
+
+
 def host_cpu_model():
     """The host's CPU model name as lscpu reports it (None if unavailable)."""
     import subprocess
@@ -517,6 +578,9 @@ def main():
         "roofline_rope_permute": rope,
         "roofline_text_attention": text,
     }
+    if args.clock:
+        res["roofline"]["clock"] = attention_clock(st, torch)
+        log(f"[bench] attention under a sampled clock: {res['roofline']['clock']}")
     if not args.no_ceilings:
         ceil = practical_ceilings(torch, w)
         ceil["attn_frac_of_gemm"] = round(attn_tfs / ceil["gemm_bf16_tflops"], 4)

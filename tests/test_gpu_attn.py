@@ -14,9 +14,9 @@ import window_attention_amd as wa
 from oracle import attention as oatt
 from oracle import permute as operm
 from oracle import plan as oplan
-from tests.gpu_helpers import MAX_ABS, MEAN_ABS, assert_close_full, check_window_head, lse_bound, lse_bound_windows, \
+from tests.gpu_helpers import MAX_ABS, MEAN_ABS, assert_close_full, lse_bound, lse_bound_windows, \
     method_of, say, to_f64
-from window_attention_amd.inputs import normal, qkv
+from window_attention_amd.inputs import bf16_bits, normal, qkv
 from window_attention_amd.workloads import WORKLOADS
 
 pytestmark = pytest.mark.gpu
@@ -186,14 +186,6 @@ def test_clip_720p_full_compare():
     assert np.all(np.abs(lse.double().cpu().numpy() - ref_lse) <= lse_bound_windows(qw_h, kw_h, op.cu_seqlens))
 
 
-def _sample_windows(cu, rng, extra=2):
-    sizes = np.diff(cu)
-    nz = np.nonzero(sizes)[0]
-    pick = {int(nz[0]), int(nz[-1]), int(nz[np.argmax(sizes[nz])]), int(nz[np.argmin(sizes[nz])])}
-    pick.update(int(x) for x in rng.choice(nz, size=min(extra, len(nz)), replace=False))
-    return sorted(pick)
-
-
 def _run_chain(w, q, k, v):
     """The benchmark's step: gather into the entry layout, then per layer a
     fused transition when the layout changes and window attention; returns
@@ -213,30 +205,51 @@ def _run_chain(w, q, k, v):
 
 
 @pytest.mark.parametrize("wi", [2, 3, 4])
-def test_full_size_workloads_sampled(wi):
+def test_full_size_workloads(wi):
+    """The benchmark's chain on the three full-size grids.  Every layer's
+    carried Q, K, V are compared in full with the canonical tensors gathered
+    by the oracle's permutation; the attention output of every window and
+    batch element is compared with the oracle for three heads (the first, the
+    last and one drawn at random; the 21x45x80 grid is compared for every
+    head in test_gpu_headline_full)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
     w = WORKLOADS[wi]
     q, k, v = qkv(w.wid, w.batch, w.L, w.heads, w.head_dim, w.sigma, device=DEV)
     layers = _run_chain(w, q, k, v)
     torch.cuda.synchronize()
     rng = np.random.default_rng(100 + wi)
+    heads = sorted({0, w.heads - 1, int(rng.integers(1, w.heads - 1))})
     for li, (lay, (qw, kw, vw), o, lse, p) in enumerate(layers):
         op = oplan.plan(w.T, w.H, w.W, w.nt, w.nh, w.nw, method_of(lay))
-        # the carried tensors are the canonical tensors in this layout, bit for bit (sampled rows vs oracle perm)
-        rows = np.unique(rng.integers(0, w.L, 2000))
+        perm = torch.as_tensor(np.asarray(op.perm, dtype=np.int64), device=DEV)
         for x_can, x_lay in ((q, qw), (k, kw), (v, vw)):
-            got = x_lay[:, torch.as_tensor(rows, device=DEV)]
-            want = x_can[:, torch.as_tensor(np.asarray(op.perm)[rows], device=DEV)]
-            assert torch.equal(got, want)
+            assert torch.equal(x_lay, x_can[:, perm])
         cu = np.asarray(op.cu_seqlens)
-        worst = (0.0, 0.0, 0.0)
-        for b in range(w.batch):
-            for i in _sample_windows(cu, rng):
-                for h in sorted({0, w.heads - 1, int(rng.integers(0, w.heads))}):
-                    mx, mean, lerr, n = check_window_head(qw, kw, vw, o, lse, cu, b, i, h)
-                    assert mx <= MAX_ABS and mean <= MEAN_ABS and lerr <= 1.0, (w.name, li, b, i, h, n, mx,
-                                                                                mean, lerr)
-                    worst = tuple(max(a, c) for a, c in zip(worst, (mx, mean, lerr)))
-        say(f"{w.name} layer {li} ({lay}): worst max={worst[0]:.3e} mean={worst[1]:.3e} lse/bound={worst[2]:.3f}")
+        hq, hk, hv, ho = (bf16_bits(x[:, :, heads]) for x in (qw, kw, vw, o))  # [B, L, 3, D]
+        hl = lse[:, heads].double().cpu().numpy()                            # [B, 3, L]
+        scale = 1.0 / math.sqrt(w.head_dim)
+
+        def block(job):
+            b, i, hi = job
+            a, e = int(cu[i]), int(cu[i + 1])
+            qh, kh, vh, oh = (oatt.bf16_bits_to_float64(x[b, a:e, hi]) for x in (hq, hk, hv, ho))
+            ref, ref_lse = oatt.head_attention(qh, kh, vh, scale)
+            err = np.abs(oh - ref)
+            lr = np.abs(hl[b, hi, a:e] - ref_lse) / lse_bound(qh, kh, scale)
+            return float(err.max()), float(err.sum()), err.size, float(lr.max())
+
+        jobs = [(b, i, hi) for b in range(w.batch) for i in range(len(cu) - 1) if cu[i + 1] > cu[i]
+                for hi in range(len(heads))]
+        with threadpool_limits(limits=2), ThreadPoolExecutor(max_workers=8) as ex:
+            res = list(ex.map(block, jobs))
+        mx = max(r[0] for r in res)
+        mean = sum(r[1] for r in res) / sum(r[2] for r in res)
+        lr = max(r[3] for r in res)
+        say(f"{w.name} layer {li} ({lay}): {len(jobs)} (batch, window, head) blocks, heads {heads}: max {mx:.3e} "
+            f"mean {mean:.3e} lse/bound {lr:.3f}")
+        assert mx <= MAX_ABS and mean <= MEAN_ABS and lr <= 1.0, (w.name, li, mx, mean, lr)
 
 
 def test_batch_invariance_hd_grid():
