@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the practical-ceiling measurements (vendor GEMM and plain copy)")
+    ap.add_argument("--attn-segments", default=None, metavar="NxLEN",
+                    help="also time win_attn_fwd alone on N equal synthetic windows of LEN rows (the workload's heads "
+                         "and head_dim), e.g. 4x8192: the kernel's rate where per-window costs vanish")
     ap.add_argument("--clock", action="store_true",
                     help="also sample the shader clock (rocm-smi, read-only) while each attention layer runs in a loop")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -365,6 +368,35 @@ def attention_clock(st, torch, seconds=2.0):
     return out
 
 
+def attention_on_segments(st, torch, spec, reps=10):
+    """win_attn_fwd alone on `spec` = "NxLEN" equal windows of synthetic
+    N(0,1) rows with the workload's heads and head_dim: TFLOP/s of the best of
+    five timed loops of `reps` calls."""
+    from window_attention_amd.inputs import normal
+    wa, w = st.wa, st.w
+    n, length = (int(x) for x in spec.lower().split("x"))
+    L = n * length
+    q, k, v = (normal((1, L, w.heads, w.head_dim), 7000 + t, device="cuda") for t in range(3))
+    cu = torch.arange(0, L + 1, length, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    for _ in range(3):
+        wa.attn_fwd(q, k, v, cu, length, out=o)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(5):
+        a.record(st.stream)
+        for _ in range(reps):
+            wa.attn_fwd(q, k, v, cu, length, out=o)
+        b.record(st.stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        best = ms if best is None else min(best, ms)
+    flops = 4 * n * length * length * w.head_dim * w.heads
+    return {"windows": n, "rows": length, "heads": w.heads, "head_dim": w.head_dim, "ms": round(best, 4),
+            "tflops": round(flops / (best * 1e-3) / 1e12, 1),
+            "frac": round(flops / (best * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS, 4)}
+
+
 def host_cpu_model():
     """The host's CPU model name as lscpu reports it (None if unavailable)."""
     import subprocess
@@ -578,6 +610,9 @@ def main():
         "roofline_rope_permute": rope,
         "roofline_text_attention": text,
     }
+    if args.attn_segments:
+        res["attn_segments"] = attention_on_segments(st, torch, args.attn_segments)
+        log(f"[bench] attention alone on {args.attn_segments} equal windows: {res['attn_segments']}")
     if args.clock:
         res["roofline"]["clock"] = attention_clock(st, torch)
         log(f"[bench] attention under a sampled clock: {res['roofline']['clock']}")
