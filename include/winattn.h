@@ -130,7 +130,8 @@ int win_plan(int32_t T, int32_t H, int32_t W, int32_t nt, int32_t nh, int32_t nw
  *   row_elems * element size must be a multiple of 16 bytes.  With L == 0
  *   nothing is read or written and the pointers may be NULL.
  * Bit-exact copy.  Errors: WIN_EINVAL, WIN_EUNSUPPORTED (dtype, row size,
- * alignment), WIN_EOVERFLOW (batch*L*row_bytes/16 >= 2^32), WIN_EDEVICE.
+ * alignment), WIN_EOVERFLOW (L or batch * L >= 2^31, row_elems >= 2^33, or
+ * batch * L rows of more than 2^62 bytes), WIN_EDEVICE.
  */
 int win_permute(const void* src, void* dst, const int32_t* idx, int64_t L, int32_t batch, int64_t row_elems,
                 int32_t dtype, int32_t mode, void* stream);
@@ -169,8 +170,9 @@ int win_transition(const void* src, void* dst, const int32_t* inv_src, const int
  * bf16 output rounded to nearest even.  Deterministic: no atomics, a fixed
  * reduction order per output row, independent of batch size and grid.
  * Errors: WIN_EINVAL, WIN_EUNSUPPORTED (head_dim, alignment), WIN_EOVERFLOW
- * (L >= 2^31, batch * num_windows * heads >= 2^31, or heads * head_dim >=
- * 2^24, so that 64 rows span 2^31 bytes or more), WIN_EDEVICE.
+ * (L >= 2^31, batch * L >= 2^38, batch * num_windows * heads >= 2^31, or
+ * heads * head_dim >= 2^24, so that 64 rows span 2^31 bytes or more),
+ * WIN_EDEVICE.
  */
 int win_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                  int32_t num_windows, int32_t max_seqlen, int64_t L, int32_t batch, int32_t heads,
@@ -329,7 +331,9 @@ int win_plan_a(int64_t L, int32_t ranks, const int32_t* src_perm, const int32_t*
  * (their text output attends to the text alone).  text_o and text_partial
  * must not overlap any input or output.
  * Errors: as win_attn_fwd; WIN_EINVAL also for text_len > 0 with a null text
- * pointer or num_windows == 0.
+ * pointer or num_windows == 0; WIN_EOVERFLOW also for text_len >= 2^25,
+ * batch * text_len >= 2^38, or per-window text outputs of 2^40 elements or
+ * more.
  */
 int win_attn_fwd_text(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                       int32_t num_windows, int32_t max_seqlen, int64_t L, int32_t batch, int32_t heads,

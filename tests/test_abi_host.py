@@ -153,6 +153,19 @@ def test_device_entry_points_validate_before_launch():
     Q2, K2, V2, O2 = (ctypes.c_void_p(i << 40) for i in (1, 2, 3, 4))
     assert lib.win_attn_fwd(Q2, K2, V2, O2, None, I, 1, 8, 8, 1, 1 << 17, 128, f(0.1), None) == -3
     assert lib.win_attn_fwd(Q2, K2, V2, O2, None, I, 0, 8, 8, 1, (1 << 17) - 1, 128, f(0.1), None) == 0
+    # byte counts are bounded before they are formed: batch * L < 2^38
+    assert lib.win_attn_fwd(Q2, K2, V2, O2, None, I, 1, 8, (1 << 31) - 1, 1 << 8, 1, 128, f(0.1), None) == -3
+    # text: batch * text_len < 2^38, and per-window text outputs below 2^40 elements
+    T1, T2, T3, T4, P = (ctypes.c_void_p(i << 40) for i in (5, 6, 7, 8, 9))
+    targs = lambda N, B, T: (Q2, K2, V2, O2, None, I, N, 8, 8, B, 1, 128, f(0.1), T1, T2, T3, T, T4, P, None)  # noqa
+    assert lib.win_attn_fwd_text(*targs(1, 1 << 14, 1 << 24)) == -3
+    assert lib.win_attn_fwd_text(*targs(1, 1, 1 << 25)) == -3
+    assert lib.win_attn_fwd_text(*targs(1 << 13, 1, 1 << 20)) == -3
+    # permutes and the rotated gather: row_elems < 2^33, and batch * L rows of at most 2^62 bytes
+    assert lib.win_permute(A, B, I, 10, 1, 1 << 33, 0, 0, None) == -3
+    assert lib.win_permute(Q2, K2, I, 1 << 30, 1, 1 << 32, 0, 0, None) == -3
+    assert lib.win_transition(Q2, K2, I, I, 1 << 30, 1, 1 << 32, 0, None) == -3
+    assert lib.win_permute_rope(Q2, K2, I, None, I, A, 3, 15, 27, 1 << 30, 1, 1 << 26, 128, 6, None) == -3
 
 
 @pytest.mark.parametrize("grid", [(1, 1, 20000), (3, 1, 15000), (2, 20000, 1)])

@@ -128,9 +128,11 @@ def _dtype_code(t):
     return _DTYPES[t.dtype]
 
 
-def _require_cuda(name, t, dtype=None):
+def _require_cuda(name, t, dtype=None, device=None):
     if not t.is_cuda:
         raise WinAttnError(-1, f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise WinAttnError(-1, f"{name} is on {t.device}, the call runs on {device}")
     if not t.is_contiguous():
         raise WinAttnError(-1, f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -351,14 +353,15 @@ def _permute_rope(src, idx, perm_dst, local, table, p: Plan, rope_dim, out):
     if table.numel() != want:
         raise WinAttnError(-1, f"table must hold (wt+wh+ww)*(rope_dim//3)={want} floats, got {table.numel()}")
     _require_cuda("src", src, torch.bfloat16)
+    dev = src.device
     for name, t in (("idx", idx), ("local", local)):
-        _require_cuda(name, t, torch.int32)
+        _require_cuda(name, t, torch.int32, dev)
     if perm_dst is not None:
-        _require_cuda("perm_dst", perm_dst, torch.int32)
-    _require_cuda("table", table, torch.float32)
+        _require_cuda("perm_dst", perm_dst, torch.int32, dev)
+    _require_cuda("table", table, torch.float32, dev)
     if out is None:
         out = torch.empty_like(src)
-    _require_cuda("out", out, torch.bfloat16)
+    _require_cuda("out", out, torch.bfloat16, dev)
     if out.shape != src.shape:
         raise WinAttnError(-1, "out must have the shape of src")
     _check(lib.win_permute_rope(_ptr(src), _ptr(out), _ptr(idx), _ptr(perm_dst), _ptr(local), _ptr(table), p.wt,
@@ -389,13 +392,13 @@ def _permute(src, idx, mode, out):
     import torch
     lib = load_library()
     _require_cuda("src", src)
-    _require_cuda("idx", idx, torch.int32)
+    _require_cuda("idx", idx, torch.int32, src.device)
     B, L, row = _rows(src)
     if idx.numel() != L:
         raise WinAttnError(-1, f"index has {idx.numel()} entries, expected L={L}")
     if out is None:
         out = torch.empty_like(src)
-    _require_cuda("out", out, src.dtype)
+    _require_cuda("out", out, src.dtype, src.device)
     if out.shape != src.shape:
         raise WinAttnError(-1, "out must have the shape of src")
     _check(lib.win_permute(_ptr(src), _ptr(out), _ptr(idx), L, B, row, _dtype_code(src), mode, _stream(src)),
@@ -418,14 +421,14 @@ def transition(src, inv_src, perm_dst, out=None):
     import torch
     lib = load_library()
     _require_cuda("src", src)
-    _require_cuda("inv_src", inv_src, torch.int32)
-    _require_cuda("perm_dst", perm_dst, torch.int32)
+    _require_cuda("inv_src", inv_src, torch.int32, src.device)
+    _require_cuda("perm_dst", perm_dst, torch.int32, src.device)
     B, L, row = _rows(src)
     if inv_src.numel() != L or perm_dst.numel() != L:
         raise WinAttnError(-1, "index tables must have L entries")
     if out is None:
         out = torch.empty_like(src)
-    _require_cuda("out", out, src.dtype)
+    _require_cuda("out", out, src.dtype, src.device)
     if out.shape != src.shape:
         raise WinAttnError(-1, "out must have the shape of src")
     _check(lib.win_transition(_ptr(src), _ptr(out), _ptr(inv_src), _ptr(perm_dst), L, B, row, _dtype_code(src),
@@ -441,16 +444,16 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, out=None, retu
     import torch
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _require_cuda(name, t, torch.bfloat16)
+        _require_cuda(name, t, torch.bfloat16, q.device)
         if t.dim() != 4 or t.shape != q.shape:
             raise WinAttnError(-1, f"{name} must be [B, L, heads, head_dim] like q")
-    _require_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    _require_cuda("cu_seqlens", cu_seqlens, torch.int32, q.device)
     B, L, Hh, D = q.shape
     if softmax_scale is None:
         softmax_scale = 0.0  # the library's default, 1/sqrt(head_dim)
     if out is None:
         out = torch.empty_like(q)
-    _require_cuda("out", out, torch.bfloat16)
+    _require_cuda("out", out, torch.bfloat16, q.device)
     if out.shape != q.shape:
         raise WinAttnError(-1, "out must have the shape of q")
     lse = torch.empty((B, Hh, L), dtype=torch.float32, device=q.device) if return_lse else None
@@ -469,15 +472,15 @@ def attn_fwd_text(q, k, v, cu_seqlens, max_seqlen, text_q, text_k, text_v, softm
     import torch
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _require_cuda(name, t, torch.bfloat16)
+        _require_cuda(name, t, torch.bfloat16, q.device)
         if t.dim() != 4 or t.shape != q.shape:
             raise WinAttnError(-1, f"{name} must be [B, L, heads, head_dim] like q")
     B, L, Hh, D = q.shape
     for name, t in (("text_q", text_q), ("text_k", text_k), ("text_v", text_v)):
-        _require_cuda(name, t, torch.bfloat16)
+        _require_cuda(name, t, torch.bfloat16, q.device)
         if t.dim() != 4 or t.shape != text_q.shape or t.shape[0] != B or t.shape[2:] != q.shape[2:]:
             raise WinAttnError(-1, f"{name} must be [B, text_len, heads, head_dim] like text_q")
-    _require_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    _require_cuda("cu_seqlens", cu_seqlens, torch.int32, q.device)
     T = text_q.shape[1]
     N = cu_seqlens.numel() - 1
     if softmax_scale is None:
@@ -488,9 +491,9 @@ def attn_fwd_text(q, k, v, cu_seqlens, max_seqlen, text_q, text_k, text_v, softm
         text_out = torch.empty_like(text_q)
     if workspace is None:
         workspace = torch.empty((B, max(N, 0), T, Hh, D), dtype=torch.float32, device=q.device)
-    _require_cuda("out", out, torch.bfloat16)
-    _require_cuda("text_out", text_out, torch.bfloat16)
-    _require_cuda("workspace", workspace, torch.float32)
+    _require_cuda("out", out, torch.bfloat16, q.device)
+    _require_cuda("text_out", text_out, torch.bfloat16, q.device)
+    _require_cuda("workspace", workspace, torch.float32, q.device)
     if out.shape != q.shape or text_out.shape != text_q.shape or workspace.numel() < B * N * T * Hh * D:
         raise WinAttnError(-1, "out, text_out or workspace has the wrong size")
     lse = torch.empty((B, Hh, L), dtype=torch.float32, device=q.device) if return_lse else None
@@ -510,25 +513,25 @@ def attn_fwd_text_noalloc(q, k, v, cu_seqlens, max_seqlen, text_q, text_k, text_
     import torch
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _require_cuda(name, t, torch.bfloat16)
+        _require_cuda(name, t, torch.bfloat16, q.device)
         if t.dim() != 4 or t.shape != q.shape:
             raise WinAttnError(-1, f"{name} must be [B, L, heads, head_dim] like q")
     B, L, Hh, D = q.shape
     for name, t in (("text_q", text_q), ("text_k", text_k), ("text_v", text_v)):
-        _require_cuda(name, t, torch.bfloat16)
+        _require_cuda(name, t, torch.bfloat16, q.device)
         if t.dim() != 4 or t.shape != text_q.shape or t.shape[0] != B or t.shape[2:] != q.shape[2:]:
             raise WinAttnError(-1, f"{name} must be [B, text_len, heads, head_dim] like text_q")
-    _require_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    _require_cuda("cu_seqlens", cu_seqlens, torch.int32, q.device)
     if out is None:
         out = torch.empty_like(q)
     if text_out is None:
         text_out = torch.empty_like(text_q)
-    _require_cuda("out", out, torch.bfloat16)
-    _require_cuda("text_out", text_out, torch.bfloat16)
+    _require_cuda("out", out, torch.bfloat16, q.device)
+    _require_cuda("text_out", text_out, torch.bfloat16, q.device)
     if out.shape != q.shape or text_out.shape != text_q.shape:
         raise WinAttnError(-1, "out or text_out has the wrong shape")
     if lse is not None:
-        _require_cuda("lse", lse, torch.float32)
+        _require_cuda("lse", lse, torch.float32, q.device)
         if lse.shape != (B, Hh, L):
             raise WinAttnError(-1, "lse must be [B, heads, L]")
     scale = 0.0 if softmax_scale is None else float(softmax_scale)

@@ -938,6 +938,10 @@ int attn_impl(const void* q, const void* k, const void* v, void* o, float* lse, 
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return WIN_EUNSUPPORTED;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return WIN_EUNSUPPORTED;
     if (L >= ((int64_t)1 << 31) || max_seqlen > L) return max_seqlen > L ? WIN_EINVAL : WIN_EOVERFLOW;
+    // a key tile's rows are addressed with 32-bit buffer offsets; with that,
+    // batch * L < 2^38 keeps every byte count below 2^63
+    if ((int64_t)kBN * heads * head_dim * 2 >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
+    if ((int64_t)batch * L >= ((int64_t)1 << 38)) return WIN_EOVERFLOW;
     const int64_t elems = (int64_t)batch * L * heads * head_dim;
     const uint64_t bytes = (uint64_t)elems * 2;
     if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
@@ -945,15 +949,18 @@ int attn_impl(const void* q, const void* k, const void* v, void* o, float* lse, 
     if (lse && overlaps(lse, (uint64_t)batch * heads * L * 4, o, bytes)) return WIN_EINVAL;
     const int64_t pairs = (int64_t)batch * num_windows * heads;
     if (pairs >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
-    // a key tile's rows are addressed with 32-bit buffer offsets
-    if ((int64_t)kBN * heads * head_dim * 2 >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
+    // batch * text_len < 2^38 and heads * head_dim < 2^24 keep t_elems below
+    // 2^62; the per-window text outputs are bounded by 2^40 elements before
+    // their count is formed
+    if (text_len >= ((int64_t)1 << 31) / 64 || (int64_t)batch * text_len >= ((int64_t)1 << 38))
+        return WIN_EOVERFLOW;
     const int64_t t_elems = (int64_t)batch * text_len * heads * head_dim;
+    if (text_len > 0 && num_windows > (((int64_t)1 << 40) - 1) / t_elems) return WIN_EOVERFLOW;
     const int64_t p_elems = t_elems * num_windows;
     if (text_len > 0) {
         if (!tq || !tk || !tv || !text_o || !text_partial || num_windows == 0) return WIN_EINVAL;
         if (!aligned16(tq) || !aligned16(tk) || !aligned16(tv) || !aligned16(text_o) || !aligned16(text_partial))
             return WIN_EUNSUPPORTED;
-        if (text_len >= ((int64_t)1 << 31) / 64 || p_elems >= ((int64_t)1 << 40)) return WIN_EOVERFLOW;
         const uint64_t tb = (uint64_t)t_elems * 2, pb = (uint64_t)p_elems * 4;
         const void* ins[6] = {q, k, v, tq, tk, tv};
         for (const void* x : ins) {

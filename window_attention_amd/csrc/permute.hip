@@ -80,11 +80,13 @@ int check_rows(const void* src, void* dst, int64_t L, int32_t batch, int64_t row
     }
     if (!src || !dst) return WIN_EINVAL;
     if (!aligned16(src) || !aligned16(dst)) return WIN_EUNSUPPORTED;
+    if (L >= ((int64_t)1 << 31) || row_elems >= ((int64_t)1 << 33)) return WIN_EOVERFLOW;
     const int64_t row_bytes = row_elems * eb;
     if (row_bytes % 16) return WIN_EUNSUPPORTED;
-    if (L >= ((int64_t)1 << 31) || row_bytes / 16 >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
+    if (row_bytes / 16 >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
     const int64_t nrows = L * batch;
     if (nrows >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
+    if (row_bytes > ((int64_t)1 << 62) / nrows) return WIN_EOVERFLOW;  // tensor bytes stay below 2^62
     if (overlaps(src, (uint64_t)(nrows * row_bytes), dst, (uint64_t)(nrows * row_bytes))) return WIN_EINVAL;
     *rows = (uint32_t)nrows;
     *cpr = (uint32_t)(row_bytes / 16);

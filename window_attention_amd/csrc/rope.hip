@@ -154,6 +154,7 @@ extern "C" int win_permute_rope(const void* src, void* dst, const int32_t* idx, 
     const int64_t row_bytes = (int64_t)heads * head_dim * 2;
     const int64_t nrows = L * batch;
     if (nrows >= ((int64_t)1 << 31) || row_bytes / 16 >= ((int64_t)1 << 31)) return WIN_EOVERFLOW;
+    if (row_bytes > ((int64_t)1 << 62) / nrows) return WIN_EOVERFLOW;  // tensor bytes stay below 2^62
     if (overlaps(src, (uint64_t)(nrows * row_bytes), dst, (uint64_t)(nrows * row_bytes))) return WIN_EINVAL;
     RopeArgs a;
     a.src = static_cast<const u32x4*>(src);
