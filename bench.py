@@ -47,6 +47,8 @@ def parse():
                          "and head_dim), e.g. 4x8192: the kernel's rate where per-window costs vanish")
     ap.add_argument("--clock", action="store_true",
                     help="also sample the shader clock (rocm-smi, read-only) while each attention layer runs in a loop")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (one capture, then --steps replays)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain device-to-device copy of one workload tensor (the reference kernel of "
                          "known size for HBM byte counters)")
@@ -150,6 +152,37 @@ class Step:
                 self.attn_events.append((a, b))
         pl = self.plans[cur]
         perm_launch(lambda: wa.scatter(self.o, pl.perm, out=self.out))
+
+
+def graph_step_rate(st, torch, steps):
+    """The same step captured once into a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: no host launch work per kernel.  The replayed step's output is
+    compared bit for bit with the eager step's."""
+    st.run()
+    torch.cuda.synchronize()
+    eager_out = st.out.clone()
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.run()  # warm-up on the capture's side stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run()
+    st.out.fill_(7.0)
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(st.out, eager_out))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    return {"ms_per_step": round(ms, 4), "value": round(sum(st.attn_flops) / (ms * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s", "bit_identical_to_eager": same}
 
 
 def rope_gather_rate(st, torch, reps=20, text_len=58):
@@ -610,6 +643,9 @@ def main():
         "roofline_rope_permute": rope,
         "roofline_text_attention": text,
     }
+    if args.graph:
+        res["graph"] = graph_step_rate(st, torch, args.steps)
+        log(f"[bench] step replayed from a HIP graph: {res['graph']}")
     if args.attn_segments:
         res["attn_segments"] = attention_on_segments(st, torch, args.attn_segments)
         log(f"[bench] attention alone on {args.attn_segments} equal windows: {res['attn_segments']}")
