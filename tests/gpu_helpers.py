@@ -48,6 +48,32 @@ def lse_bound(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
     return score + norm + final
 
 
+def output_bound(q: np.ndarray, k: np.ndarray, o_ref: np.ndarray, pv_abs: np.ndarray, scale: float) -> np.ndarray:
+    """Per-element bound on |O_gpu - O| for one segment and head, from the
+    kernel's arithmetic, for values of any magnitude: q [n, D], k [m, D],
+    o_ref [n, Dv] the exact output and pv_abs [n, Dv] = sum_k p_k |v_k| (the
+    oracle applied to |V|).
+      * P V takes bf16 roundings of the fp32 probabilities: 2^-8 relative
+        each, so 2^-8 * sum_k p_k |v_k|;
+      * the fp32 probabilities themselves: the score terms of lse_bound
+        (relative error of each p_k), the normaliser's chain of adds and
+        reference moves (relative error of the row sum, hence of O);
+      * the fp32 P V accumulation over m keys, n_tiles deferred rescales
+        (an exp2 factor and a product each) and the final 1 / l product:
+        m * 2^-24 + tiles * 2^-20 + 2^-22 relative to sum_k p_k |v_k|;
+      * the bf16 rounding of the output: 2^-8 relative to the computed value.
+    """
+    D = q.shape[1]
+    m = k.shape[0]
+    s_abs = np.abs(q @ k.T) * scale
+    score = (D * 2.0 ** -23 * scale * (np.abs(q) @ np.abs(k).T) + 2.0 ** -22 * s_abs).max(axis=1) + 2.0 ** -18
+    tiles = math.ceil(m / KEY_TILE) + 1
+    norm = 2.0 ** -21 + (32 + tiles + 2) * 2.0 ** -24 + tiles * (2.0 ** -21 + 2.0 ** -24)
+    acc = m * 2.0 ** -24 + tiles * 2.0 ** -20 + 2.0 ** -22
+    rel = 2.0 ** -8 + np.expm1(score)[:, None] + norm + acc
+    return 2.0 ** -8 * np.abs(o_ref) + (1 + 2.0 ** -8) * rel * pv_abs
+
+
 def lse_bound_windows(q, k, cu, scale=None):
     """lse_bound for [B, L, Hh, D] window-ordered inputs, as [B, Hh, L]."""
     B, L, Hh, D = q.shape

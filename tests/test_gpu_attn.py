@@ -15,7 +15,7 @@ from oracle import attention as oatt
 from oracle import permute as operm
 from oracle import plan as oplan
 from tests.gpu_helpers import MAX_ABS, MEAN_ABS, assert_close_full, lse_bound, lse_bound_windows, \
-    method_of, say, to_f64
+    method_of, output_bound, say, to_f64
 from window_attention_amd.inputs import bf16_bits, normal, qkv
 from window_attention_amd.workloads import WORKLOADS
 
@@ -64,6 +64,42 @@ def test_softmax_scale(D, scale):
     qh, kh = to_f64(q), to_f64(k)
     ref_o, ref_lse = oatt.window_attention(qh, kh, to_f64(v), cu, scale)
     assert_close_full(o, lse, ref_o, ref_lse, lse_bound_windows(qh, kh, cu, scale))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("sigma,offset", [(16.0, 0.0), (256.0, 0.0), (1.0, 1000.0)])
+def test_large_magnitude_values(D, sigma, offset):
+    """V far from unit scale (standard deviation 16 or 256, or 1000 plus unit
+    noise), where an absolute tolerance says nothing: every element of O
+    against the oracle within output_bound, a bound from the kernel's
+    arithmetic that scales with |O| and with sum_k p_k |v_k| (the oracle's
+    attention applied to |V|).  The LSE does not depend on V and keeps its
+    own bound."""
+    say(f"large values D={D} sigma={sigma} offset={offset}")
+    lengths = [1, 65, 700, 2430]
+    cu = _cu(lengths)
+    L, B, Hh = int(cu[-1]), 1, 2
+    q, k = (normal((B, L, Hh, D), 540 + t, device=DEV) for t in range(2))
+    v = (normal((B, L, Hh, D), 542, device=DEV).float() * sigma + offset).to(torch.bfloat16)
+    o, lse = wa.attn_fwd(q, k, v, torch.as_tensor(cu, device=DEV), max(lengths), return_lse=True)
+    qh, kh, vh = to_f64(q), to_f64(k), to_f64(v)
+    ref_o, ref_lse = oatt.window_attention(qh, kh, vh, cu)
+    pv_abs, _ = oatt.window_attention(qh, kh, np.abs(vh), cu)
+    got = to_f64(o)
+    scale = 1.0 / math.sqrt(D)
+    worst = 0.0
+    for b in range(B):
+        for i in range(len(lengths)):
+            a, e = int(cu[i]), int(cu[i + 1])
+            for h in range(Hh):
+                bound = output_bound(qh[b, a:e, h], kh[b, a:e, h], ref_o[b, a:e, h], pv_abs[b, a:e, h], scale)
+                err = np.abs(got[b, a:e, h] - ref_o[b, a:e, h])
+                assert np.all(err <= bound), f"window {i} head {h}: worst ratio {(err / bound).max():.3f}"
+                worst = max(worst, float((err / bound).max()))
+    le = np.abs(lse.double().cpu().numpy() - ref_lse)
+    assert np.all(le <= lse_bound_windows(qh, kh, cu))
+    say(f"  max |O| {np.abs(ref_o).max():.1f}, max abs err {np.abs(got - ref_o).max():.3g}, "
+        f"worst error / bound {worst:.3f}")
 
 
 def _steer_scores(q, k, cu, pattern):
