@@ -308,7 +308,7 @@ def measured_traffic(kernel_prefix, workload):
 
 
 def practical_ceilings(torch, w, reps=20):
-    """What this box sustains, measured here beside the path (context only, not
+    """What this machine sustains, measured here beside the path (context only, not
     part of it): a vendor dense bf16 GEMM on N(0,1) data, whose power-limited
     clock is the practical ceiling of an MFMA-bound kernel on real data, and a
     plain device copy of one workload-sized tensor, the practical ceiling of a
