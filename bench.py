@@ -328,6 +328,7 @@ def practical_ceilings(torch, w, reps=20):
     gemm_tfs = 2 * n ** 3 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
     del a, c
     x = torch.empty((w.batch, w.L, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    x_bytes = x.numel() * 2
     y = torch.empty_like(x)
     for _ in range(3):
         y.copy_(x)
@@ -338,8 +339,47 @@ def practical_ceilings(torch, w, reps=20):
     e1.record()
     torch.cuda.synchronize()
     copy_gbs = 2 * x.numel() * 2 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
-    return {"gemm_bf16_tflops": round(gemm_tfs, 1), "gemm": f"torch.matmul bf16 {n}x{n}x{n}, N(0,1) data",
-            "copy_gbps": round(copy_gbs, 1), "copy": f"device copy of {x.numel() * 2} bytes"}
+    del x, y
+    res = {"gemm_bf16_tflops": round(gemm_tfs, 1), "gemm": f"torch.matmul bf16 {n}x{n}x{n}, N(0,1) data",
+           "copy_gbps": round(copy_gbs, 1), "copy": f"device copy of {x_bytes} bytes"}
+    res.update(mfma_loop_rate(torch))
+    return res
+
+
+def mfma_loop_rate(torch, reps=10, iters=32768):
+    """The chip's sustained bf16 MFMA rate on changing N(0,1) register data
+    (libwinprobe.so: eight independent 32x32x16 chains per wave, two
+    workgroups of four waves per CU, no memory traffic in the loop): the
+    ceiling of any kernel's MFMA work under the power limit."""
+    import ctypes
+    path = os.path.join(ROOT, "window_attention_amd", "libwinprobe.so")
+    if not os.path.exists(path):
+        return {"mfma_loop_tflops": None, "mfma_loop": "libwinprobe.so not built"}
+    lib = ctypes.CDLL(path)
+    lib.win_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p]
+    lib.win_probe_mfma_loop.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * cus
+    src = torch.randn(1 << 19, device="cuda").to(torch.bfloat16)
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    call = lambda: lib.win_probe_mfma_loop(src.data_ptr(), src.numel(), out.data_ptr(), blocks, iters, st)  # noqa
+    for _ in range(2):
+        if call() != 0:
+            return {"mfma_loop_tflops": None, "mfma_loop": "launch failed"}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = blocks * 4 * 8 * ((iters + 3) // 4 * 4) * 32768
+    return {"mfma_loop_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_loop": f"{blocks} workgroups x 4 waves x 8 chains of mfma_f32_32x32x16_bf16 on N(0,1) "
+                         f"register operands, {iters} per chain"}
 
 
 def sample_sclk(stop, out):
@@ -656,9 +696,12 @@ def main():
         ceil = practical_ceilings(torch, w)
         ceil["attn_frac_of_gemm"] = round(attn_tfs / ceil["gemm_bf16_tflops"], 4)
         ceil["permute_frac_of_copy"] = round(perm_gbs / ceil["copy_gbps"], 4)
+        if ceil.get("mfma_loop_tflops"):
+            ceil["attn_frac_of_mfma_loop"] = round(attn_tfs / ceil["mfma_loop_tflops"], 4)
         log(f"[bench] practical ceilings: vendor bf16 GEMM {ceil['gemm_bf16_tflops']} TFLOP/s "
             f"(attention at {ceil['attn_frac_of_gemm']:.2f} of it), device copy {ceil['copy_gbps']} GB/s "
-            f"(permutes at {ceil['permute_frac_of_copy']:.2f} of it)")
+            f"(permutes at {ceil['permute_frac_of_copy']:.2f} of it), MFMA loop on N(0,1) registers "
+            f"{ceil.get('mfma_loop_tflops')} TFLOP/s (attention at {ceil.get('attn_frac_of_mfma_loop')} of it)")
         res["practical_ceilings"] = ceil
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle sample, about {args.cpu_seconds:.0f} s")

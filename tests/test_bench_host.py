@@ -39,3 +39,24 @@ def test_traffic_records_parse_and_name_their_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("foo_kernel", "other") is None
     src.write_text("kernel source, changed\n")
     assert bench.measured_traffic("foo_kernel", "w") is None
+
+
+def test_mfma_probe_library_validates_before_launch():
+    """libwinprobe.so (bench.py's MFMA-loop ceiling) is built beside the
+    library and refuses bad arguments without touching a device (fake
+    pointers, never dereferenced)."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "window_attention_amd",
+                        "libwinprobe.so")
+    assert os.path.exists(path), "build() writes libwinprobe.so"
+    lib = ctypes.CDLL(path)
+    f = lib.win_probe_mfma_loop
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    S, O = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+    assert f(None, 1024, O, 1, 4, None) == -1
+    assert f(S, 1024, None, 1, 4, None) == -1
+    assert f(S, 1020, O, 1, 4, None) == -1          # not a whole number of 8-element fragments
+    assert f(S, 1024, O, 0, 4, None) == -1
+    assert f(S, 1024, O, 1, 0, None) == -1
+    assert f(ctypes.c_void_p(0x10008), 1024, O, 1, 4, None) == -1  # misaligned

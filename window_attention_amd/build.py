@@ -1,4 +1,5 @@
-"""Build libwinattn.so in-tree with hipcc for gfx950.
+"""Build libwinattn.so (and the measurement library libwinprobe.so) in-tree
+with hipcc for gfx950.
 
 Run as ``python -m window_attention_amd.build``; ``__graft_entry__.build()``
 calls ``build()``.  Every call recompiles from source.
@@ -16,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwinattn.so")
+# measurement beside the path (bench.py's practical ceilings), a library of its own
+PROBE_LIB = os.path.join(PKG, "libwinprobe.so")
+PROBE_SOURCE = "mfma_probe.hip"
 ARCH = "gfx950"
 
 # packed fp32 VALU forms are switched off for all device code
@@ -67,6 +71,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *[j[0] for j in jobs], "-o", tmp])
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc, *COMMON, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", tmp])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
