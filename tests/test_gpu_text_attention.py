@@ -10,7 +10,7 @@ import torch
 import window_attention_amd as wa
 from oracle import attention as oatt
 from oracle import text_attention as otxt
-from tests.gpu_helpers import MAX_ABS, MEAN_ABS, lse_bound, say, to_f64
+from tests.gpu_helpers import MAX_ABS, MEAN_ABS, lse_bound, output_bound, say, to_f64
 from window_attention_amd.inputs import normal, qkv
 
 pytestmark = pytest.mark.gpu
@@ -62,6 +62,55 @@ def test_small_full_compare(D, lengths, T):
                 _, ref_lse = oatt.head_attention(qh[b, a:e, h], ks, vs, s)
                 got = lse[b, h, a:e].double().cpu().numpy()
                 assert np.all(np.abs(got - ref_lse) <= lse_bound(qh[b, a:e, h], ks, s))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_large_magnitude_values_with_text(D):
+    """Window and text values of standard deviation 256: video rows and the
+    fp32 per-window text outputs against output_bound over each segment's
+    keys, and the text output against the mean of those bounds plus the fp32
+    sum over the windows (N + 1 roundings of 2^-24 relative to the mean of
+    |per-window output|) and its bf16 rounding (2^-8 relative)."""
+    say(f"large values with text D={D}")
+    B, Hh, T, sigma = 1, 2, 77, 256.0
+    lengths = [1, 65, 700]
+    cu = _cu(lengths)
+    L, N = int(cu[-1]), len(lengths)
+    q, k = (normal((B, L, Hh, D), 560 + t, device=DEV) for t in range(2))
+    v = (normal((B, L, Hh, D), 562, device=DEV).float() * sigma).to(torch.bfloat16)
+    tq, tk = (normal((B, T, Hh, D), 570 + t, device=DEV) for t in range(2))
+    tv = (normal((B, T, Hh, D), 572, device=DEV).float() * sigma).to(torch.bfloat16)
+    ws = torch.full((B, N, T, Hh, D), float("nan"), dtype=torch.float32, device=DEV)
+    o, to = wa.attn_fwd_text(q, k, v, torch.as_tensor(cu, device=DEV), max(lengths), tq, tk, tv, workspace=ws)
+    torch.cuda.synchronize()
+    qh, kh, vh, tqh, tkh, tvh = (to_f64(x) for x in (q, k, v, tq, tk, tv))
+    ref_o, ref_t, ref_per = otxt.text_window_attention(qh, kh, vh, cu.tolist(), tqh, tkh, tvh)
+    abs_o, _, abs_per = otxt.text_window_attention(qh, kh, np.abs(vh), cu.tolist(), tqh, tkh, np.abs(tvh))
+    got_o, got_t, got_per = to_f64(o), to_f64(to), ws.double().cpu().numpy()
+    s = 1 / math.sqrt(D)
+    worst = 0.0
+    for b in range(B):
+        for h in range(Hh):
+            per_bounds = []
+            for i in range(N):
+                a, e = int(cu[i]), int(cu[i + 1])
+                ks = np.concatenate([kh[b, a:e, h], tkh[b, :, h]])
+                if e > a:
+                    bd = output_bound(qh[b, a:e, h], ks, ref_o[b, a:e, h], abs_o[b, a:e, h], s)
+                    err = np.abs(got_o[b, a:e, h] - ref_o[b, a:e, h])
+                    assert np.all(err <= bd), ("video", i, h, float((err / bd).max()))
+                    worst = max(worst, float((err / bd).max()))
+                bt = output_bound(tqh[b, :, h], ks, ref_per[b, i, :, h], abs_per[b, i, :, h], s)
+                err = np.abs(got_per[b, i, :, h] - ref_per[b, i, :, h])
+                assert np.all(err <= bt), ("per-window text", i, h, float((err / bt).max()))
+                per_bounds.append(bt)
+            mean_abs = np.mean([np.abs(ref_per[b, i, :, h]) for i in range(N)], axis=0)
+            bound_t = np.mean(per_bounds, axis=0) * (1 + 2.0 ** -8) + (N + 1) * 2.0 ** -24 * mean_abs \
+                + 2.0 ** -8 * np.abs(ref_t[b, :, h])
+            err = np.abs(got_t[b, :, h] - ref_t[b, :, h])
+            assert np.all(err <= bound_t), ("text", h, float((err / bound_t).max()))
+            worst = max(worst, float((err / bound_t).max()))
+    say(f"  max |text out| {np.abs(ref_t).max():.1f}, worst error / bound {worst:.3f}")
 
 
 @pytest.mark.parametrize("scale", [0.05, 0.5])
